@@ -1,0 +1,30 @@
+"""Oracle: a plain, slow CPU implementation of the fused block, used to check the GPU path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import anything from this package.  The
+library (``chunked_matmul_reduce_amd``) never imports it, and this package imports
+nothing from the library: the two share no code.  Their only common input is the
+seeded generator in ``workload``, which holds none of the block's arithmetic.
+
+Contents
+* ``block``  -- the block in fp64 (numpy; products and slice GEMMs through dgemm),
+  the dropout mask, and an fp32 model of the declared rounding order;
+* ``philox`` -- Philox4x32-10 from Salmon et al. (SC'11), scalar and vectorized.
+
+Pins (all in ``tests/test_oracle.py`` and ``tests/test_philox.py``): exact rational
+brute force on tiny shapes; the slice-sum invariant against the unsliced product;
+p = 0 against a direct library product; p = 1 against the residual; closed-form inputs
+that isolate the bias, residual, scale and indexing; the kept fraction against its
+binomial spread; Philox against its constants' closed forms, against a second
+implementation, and against rocRAND's header-only Philox4x32-10 engine when a host
+compiler can build it.  Nothing on the pages prints a numeric example, so no pin comes
+from the pages themselves.
+"""
+from .block import (check_p, drop_threshold, keep_elements, keep_mask, keep_scale,
+                    reduce_epilogue_fp32, run, run_inputs, slice_bounds, slice_partials,
+                    widen)
+from . import philox
+
+__all__ = ["check_p", "drop_threshold", "keep_elements", "keep_mask", "keep_scale",
+           "reduce_epilogue_fp32", "run", "run_inputs", "slice_bounds", "slice_partials",
+           "widen", "philox"]
