@@ -1,0 +1,208 @@
+"""Benchmark of the fused MatMul -> slice-reduce -> epilogue block on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload gpt2_mlp]
+
+A step is one call of the whole block (all P slice GEMMs, the fixed-order slice
+reduction, bias + Philox dropout + residual) on one batch of seeded synthetic input
+already resident in HBM.  Default workload: the GPT-2 8.3B MLP down-projection block,
+M=8192, K=12288 split in P=16 slices, N=3072 (bf16 in, fp32 accumulate and out).
+
+One JSON line on stdout: throughput in TFLOP/s (2*M*N*K per step), the roofline of the
+dominant kernel (the persistent fused tile kernel, timed per launch with HIP events on
+the stream it runs on), the hidden fraction 1 - (T_fused - T_gemm_alone) / T_re_alone,
+and the oracle's CPU throughput on a bounded sample of the same workload.
+
+--only fused     time only the fused block (for rocprofv3 runs)
+--only copy      one plain 1 GiB device copy, the calibration point for HBM counters
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "fused GEMM+reduce+epilogue TFLOP/s, % bf16 MFMA peak, % epilogue hidden"
+
+
+def _ev_time(torch, fn, reps):
+    """Median and mean of per-call durations (ms), HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        fn()
+        e1.record(s)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
+    times.sort()
+    return times[len(times) // 2], sum(times) / len(times)
+
+
+def _traffic(kernel_sha):
+    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic_tile_kernel_fused_gpt2_mlp.json")
+    try:
+        with open(path) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernels_hip_sha256") != kernel_sha:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def _cpu_baseline(inp, w, budget_s):
+    import contextlib
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    ctx = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+    rows_done, t_total = 0, 0.0
+    block = 1024
+    with ctx:
+        while rows_done < w.M and t_total < budget_s:
+            rows = np.arange(rows_done, min(w.M, rows_done + block))
+            t0 = time.perf_counter()
+            oracle.run_inputs(inp, rows=rows)
+            t_total += time.perf_counter() - t0
+            rows_done += rows.size
+    flops = 2.0 * rows_done * w.N * w.K
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"rows 0..{rows_done - 1} of M={w.M} (all N={w.N}, K={w.K}, P={w.P}): "
+                      f"{rows_done / w.M:.0%} of the workload, fp64 numpy/OpenBLAS, "
+                      f"{t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt2_mlp")
+    ap.add_argument("--only", choices=["all", "fused", "copy"], default="all")
+    ap.add_argument("--cpu-budget", type=float, default=30.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the P ranks are folded onto one device as K-slices)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import chunked_matmul_reduce_amd as mmar
+    from workload import WORKLOADS, make_inputs
+
+    torch.cuda.set_device(0)
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}))
+        return
+
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    d = {k: torch.from_numpy(inp[k].view(np.int16)).to("cuda").view(torch.bfloat16)
+         for k in ("X", "W", "bias", "residual")}
+    X, W, bias, res = d["X"], d["W"], d["bias"], d["residual"]
+    P, p, seed = w.P, float(inp["p_drop"]), w.seed
+    out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+    plan = mmar.get_plan(w.M, w.N, w.K, P)
+
+    def fused():
+        mmar.fused(X, W, bias, res, P, p, seed, out=out)
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record(stream)
+        fused()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    kernel_ms = sum(launch_ms) / len(launch_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.desc}", "M": w.M, "K": w.K, "N": w.N, "P": P,
+                   "p_drop": p, "seed": seed, "out_dtype": "fp32", "accumulate": "fp32",
+                   "plan": {"schedule": {1: "sequential", 2: "streams", 3: "persistent"}[plan["schedule"]],
+                            "chunk": list(plan["chunk"]), "ring": plan["ring"]}},
+    }
+    with open(os.path.join(ROOT, "chunked_matmul_reduce_amd", "csrc", "kernels.hip"), "rb") as f:
+        ksha = hashlib.sha256(f.read()).hexdigest()
+    achieved = flops / (kernel_ms * 1e-3) / 1e12
+    result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                          "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                          "traffic": _traffic(ksha),
+                          "kernel": "mmar::tile_kernel<kModeFused, 64> (persistent, one launch per step)",
+                          "per_launch": f"2*M*N*K = {w.flops} flop"}
+    result["pct_bf16_peak"] = round(100 * value / PEAK_BF16_TFLOPS, 2)
+
+    if args.only == "all":
+        reps = max(10, args.steps)
+        t_fused = _ev_time(torch, fused, reps)[0]
+        T = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        t_gemm = _ev_time(torch, lambda: mmar.gemm_only(X, W, P, out=T), reps)[0]
+        parts = torch.empty((P, w.M, w.N), dtype=torch.float32, device="cuda")
+        t_parts = _ev_time(torch, lambda: mmar.gemm_partials(X, W, P, out=parts), reps)[0]
+        t_re = _ev_time(torch, lambda: mmar.reduce_epilogue_only(parts, bias, res, p, seed, out=out),
+                        reps)[0]
+        t_epi = _ev_time(torch, lambda: mmar.reduce_epilogue_only(T[None], bias, res, p, seed, out=out),
+                         reps)[0]
+        t_seq = _ev_time(torch, lambda: mmar.sequential(X, W, bias, res, P, p, seed, out=out), reps)[0]
+        t_str = _ev_time(torch, lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "streams", out=out),
+                         reps)[0]
+        del parts
+        torch.cuda.empty_cache()
+        re_bytes = (4 * P + 6) * w.M * w.N + 2 * w.N
+        epi_bytes = 10 * w.M * w.N + 2 * w.N
+        result["times_us"] = {k: round(v * 1e3, 2) for k, v in
+                              {"fused": t_fused, "gemm_alone": t_gemm, "partials_gemm": t_parts,
+                               "re_alone": t_re, "epi_alone": t_epi, "sequential": t_seq,
+                               "streams": t_str}.items()}
+        result["hidden_fraction"] = round(1.0 - (t_fused - t_gemm) / t_re, 4)
+        result["hidden_fraction_epilogue"] = round(1.0 - (t_fused - t_gemm) / t_epi, 4)
+        result["speedup_vs_sequential"] = round(t_seq / t_fused, 3)
+        result["speedup_streams_vs_sequential"] = round(t_seq / t_str, 3)
+        result["re_alone_GBps"] = round(re_bytes / (t_re * 1e-3) / 1e9, 1)
+        result["epi_alone_GBps"] = round(epi_bytes / (t_epi * 1e-3) / 1e9, 1)
+
+    if not args.no_cpu_baseline and args.only == "all":
+        result["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

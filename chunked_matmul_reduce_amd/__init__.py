@@ -1,0 +1,272 @@
+"""Python binding of libmmar, the gfx950 fused MatMul -> slice-reduce -> epilogue library.
+
+Argument marshalling only: every step of the block runs in the HIP kernels behind the C
+ABI of ``include/mmar.h``.  PyTorch supplies device memory and the current HIP stream.
+Importing this package fails if ``libmmar.so`` has not been built
+(``python -m chunked_matmul_reduce_amd.build``); there is no fallback.
+
+Block computed (see include/mmar.h for the full contract):
+    out = residual + dropout_p(bias + sum_p X[:, K_p] @ W[K_p, :])     (fp32 out)
+with bf16 X [M,K], W [K,N], bias [N], residual [M,N]; P equal K-slices; fp32 slice
+accumulation from zero; fixed-order fp32 reduction; counter-based Philox4x32-10 mask.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmmar.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mmar.h")
+
+OK, EINVAL, EALIGN, ENODEV, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
+SCHED_AUTO, SCHED_SEQUENTIAL, SCHED_STREAMS, SCHED_PERSISTENT = 0, 1, 2, 3
+SCHEDULES = {"auto": 0, "sequential": 1, "streams": 2, "persistent": 3}
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F = ctypes.c_float
+_U64 = ctypes.c_uint64
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "mmar_fused": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
+    "mmar_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    "mmar_fused_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32,
+                                     _I32, _I32, _P, _SZ, _P]),
+    "mmar_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
+    "mmar_gemm_only": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
+    "mmar_gemm_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _P]),
+    "mmar_reduce_epilogue_only": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _F, _U64, _P]),
+    "mmar_autotune": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.c_uint32]),
+    "mmar_set_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32]),
+    "mmar_get_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                     ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+    "mmar_last_error": (ctypes.c_char_p, []),
+    "mmar_version": (ctypes.c_char_p, []),
+    "mmar_release": (ctypes.c_int, []),
+}
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m chunked_matmul_reduce_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class MmarError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"mmar error {code}: {msg}")
+        self.code = code
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions include/mmar.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mmar_\w+)\s*\(", text)))
+
+
+def last_error() -> str:
+    return lib.mmar_last_error().decode()
+
+
+def version() -> str:
+    return lib.mmar_version().decode()
+
+
+def release() -> None:
+    _check(lib.mmar_release())
+
+
+def _check(rc):
+    if rc != OK:
+        raise MmarError(rc, last_error())
+
+
+# ---------------------------------------------------------------- tensor helpers
+def _torch():
+    import torch
+    return torch
+
+
+def _bits(t, name, shape):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16 (or 16-bit bf16 bit patterns), got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _f32(t, name, shape):
+    torch = _torch()
+    if t.device.type != "cuda" or t.dtype != torch.float32:
+        raise TypeError(f"{name} must be a float32 GPU tensor")
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous with shape {tuple(shape)}")
+    return t.data_ptr()
+
+
+def _stream(device, stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _out(out, shape, like):
+    torch = _torch()
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=like.device)
+    _f32(out, "out", shape)
+    return out
+
+
+def _shapes(X, W, P):
+    if X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X must be [M, K] and W [K, N]")
+    M, K = X.shape
+    K2, N = W.shape
+    if K2 != K:
+        raise ValueError(f"X is [M={M}, K={K}] but W is [{K2}, {N}]")
+    return int(M), int(N), int(K)
+
+
+# ---------------------------------------------------------------- entry points
+def fused(X, W, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, stream=None):
+    """mmar_fused: the block with the library's plan for this shape; returns fp32 out."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, P)
+    out = _out(out, (M, N), X)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_fused(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), _bits(bias, "bias", (N,)),
+                            _bits(residual, "residual", (M, N)), out.data_ptr(), M, N, K, int(P),
+                            float(p_drop), int(seed) & (2 ** 64 - 1), int(chunk[0]), int(chunk[1]),
+                            _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def fused_ex(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0), ring=0,
+             workspace=None, out=None, stream=None):
+    """mmar_fused_ex: every choice explicit; ``workspace`` is an optional uint8 GPU tensor."""
+    torch = _torch()
+    if isinstance(schedule, str):
+        schedule = SCHEDULES[schedule]
+    M, N, K = _shapes(X, W, P)
+    out = _out(out, (M, N), X)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        if workspace.device.type != "cuda" or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_fused_ex(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), _bits(bias, "bias", (N,)),
+                               _bits(residual, "residual", (M, N)), out.data_ptr(), M, N, K, int(P),
+                               float(p_drop), int(seed) & (2 ** 64 - 1), int(schedule), int(chunk[0]),
+                               int(chunk[1]), int(ring), ws_ptr, ws_bytes, _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def sequential(X, W, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, stream=None):
+    """mmar_sequential: GEMM of the partials then reduce+epilogue, no overlap."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, P)
+    out = _out(out, (M, N), X)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_sequential(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)),
+                                 _bits(bias, "bias", (N,)), _bits(residual, "residual", (M, N)),
+                                 out.data_ptr(), M, N, K, int(P), float(p_drop),
+                                 int(seed) & (2 ** 64 - 1), int(chunk[0]), int(chunk[1]),
+                                 _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def gemm_only(X, W, P, chunk=(0, 0), out=None, stream=None):
+    """mmar_gemm_only: the reduced fp32 sum T of the P slice partials (no epilogue)."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, P)
+    out = _out(out, (M, N), X)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_gemm_only(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), out.data_ptr(), M, N, K,
+                                int(P), int(chunk[0]), int(chunk[1]), _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def gemm_partials(X, W, P, out=None, stream=None):
+    """mmar_gemm_partials: the P fp32 slice partials, [P, M, N]."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, P)
+    out = _out(out, (int(P), M, N), X)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_gemm_partials(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), out.data_ptr(),
+                                    M, N, K, int(P), _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def reduce_epilogue_only(partials, bias, residual, p_drop, seed, out=None, stream=None):
+    """mmar_reduce_epilogue_only over partials [P, M, N] (fp32)."""
+    torch = _torch()
+    if partials.dim() != 3:
+        raise ValueError("partials must be [P, M, N]")
+    P, M, N = (int(v) for v in partials.shape)
+    out = _out(out, (M, N), partials)
+    with torch.cuda.device(partials.device):
+        rc = lib.mmar_reduce_epilogue_only(_f32(partials, "partials", (P, M, N)),
+                                           _bits(bias, "bias", (N,)),
+                                           _bits(residual, "residual", (M, N)), out.data_ptr(), M, N, P,
+                                           float(p_drop), int(seed) & (2 ** 64 - 1),
+                                           _stream(partials.device, stream))
+    _check(rc)
+    return out
+
+
+def workspace_bytes(schedule, M, N, K, P, chunk=(0, 0), ring=0) -> int:
+    if isinstance(schedule, str):
+        schedule = SCHEDULES[schedule]
+    n = lib.mmar_workspace_bytes(int(schedule), int(M), int(N), int(K), int(P), int(chunk[0]),
+                                 int(chunk[1]), int(ring))
+    if n == 0 and last_error():
+        raise MmarError(EINVAL, last_error())
+    return int(n)
+
+
+def autotune(M, N, K, P, flags=0) -> None:
+    _check(lib.mmar_autotune(int(M), int(N), int(K), int(P), int(flags)))
+
+
+def set_plan(M, N, K, P, schedule, chunk=(0, 0), ring=0) -> None:
+    if isinstance(schedule, str):
+        schedule = SCHEDULES[schedule]
+    _check(lib.mmar_set_plan(int(M), int(N), int(K), int(P), int(schedule), int(chunk[0]),
+                             int(chunk[1]), int(ring)))
+
+
+def get_plan(M, N, K, P):
+    s, cm, cn, r = _I32(), _I32(), _I32(), _I32()
+    _check(lib.mmar_get_plan(int(M), int(N), int(K), int(P), ctypes.byref(s), ctypes.byref(cm),
+                             ctypes.byref(cn), ctypes.byref(r)))
+    return {"schedule": s.value, "chunk": (cm.value, cn.value), "ring": r.value}

@@ -1,0 +1,401 @@
+// gfx950 kernels of the fused MatMul -> slice-reduce -> epilogue block.
+//
+// The block (CoCoNet record LIT-735, "Key takeaways": the model-parallel MatMul whose
+// partial products an AllReduce sums, overlapped in chunks, with pointwise work fused
+// into the collective) folded onto one GPU: P K-slices stand in for P ranks, and a
+// fixed-order fp32 sum of the slice partials stands in for the AllReduce.
+//
+// Tile kernel.  A 256-thread workgroup (4 waves) owns a 256 x 128 output tile.  Wave w
+// owns rows [64w, 64w+64) and all 128 columns, as 2 x 4 blocks of 32 x 32 computed with
+// v_mfma_f32_32x32x16_bf16.  The MFMA computes the transposed block (W^T in the A slot,
+// X in the B slot), so that a lane's accumulator holds one output row and, per group of
+// four registers, four consecutive columns: exactly one Philox group, one 8-byte bias /
+// residual load and one 16-byte fp32 store, with no cross-lane exchange.
+//   * X is not shared between waves (each wave owns its rows), so it goes straight from
+//     HBM/L2 into registers, double-buffered one K step ahead.
+//   * W is shared by the 4 waves: each K step's [BK x 128] tile is loaded with 8-byte
+//     row loads, transposed in registers to k-contiguous 16-byte rows and written to a
+//     double-buffered LDS tile [128][BK + 8] (the 16-byte pad makes the MFMA operand
+//     reads bank-conflict free); one barrier per K step.
+//   * Slice semantics: S (the current slice's accumulator) starts from zero at every
+//     slice boundary; at the end of a slice T = S (first slice) or T = T + S (fp32, RNE),
+//     so the partials are reduced in the fixed order p = 0..P-1 without leaving registers.
+//   * Modes: kModeFused applies bias + Philox dropout + residual to T and stores fp32
+//     out; kModeReduced stores T; kModePartials computes one slice per work item and
+//     stores S_p to a workspace.  All three share the same MFMA sequence, so partials
+//     reduced by the reduce+epilogue kernel give the same bits as the fused mode.
+//   * Work items are visited chunk by chunk, tiles inside a chunk in groups of 4 tile
+//     rows; a persistent grid walks the items with a stride of the grid size, and
+//     workgroup ids are remapped so the 32 workgroups resident on one XCD (ids are
+//     dealt round-robin over the 8 XCDs) take 32 consecutive items and share their
+//     X rows and W columns in that XCD's L2.
+//
+// Reduce+epilogue kernel.  One thread per group of four consecutive outputs: P 16-byte
+// partial loads summed left to right, then the same epilogue.  HBM-bound.
+//
+// No fused multiply-add anywhere in the epilogue (built with -ffp-contract=off and
+// written with explicit round-to-nearest add / multiply).
+#include "mmar_internal.h"
+
+namespace mmar {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// ------------------------------------------------------------------ Philox4x32-10
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11.
+// Round: the 64-bit products M0*c0 and M1*c2 split into high / low words; new counter
+// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key is bumped by the Weyl increments
+// between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
+    constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t hi0 = __umulhi(kM0, c0), lo0 = kM0 * c0;
+        const uint32_t hi1 = __umulhi(kM1, c2), lo1 = kM1 * c2;
+        const uint32_t n0 = hi1 ^ c1 ^ k0;
+        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += kW0;
+        k1 += kW1;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float epi1(float t, float b, float r, uint32_t word,
+                                      const DropParams& d) {
+    const float v = __fadd_rn(t, b);
+    const float y = __fmul_rn(v, d.scale);
+    const bool keep = (d.drop_all == 0u) && (word >= d.thr);
+    return keep ? __fadd_rn(r, y) : r;
+}
+
+// Epilogue of four consecutive outputs starting at linear index e (e % 4 == 0).
+__device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int64_t e,
+                                            const DropParams& d) {
+    const uint64_t g = static_cast<uint64_t>(e) >> 2;
+    const uint4 w = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32),
+                                  0u, 0u, d.key0, d.key1);
+    float4 o;
+    o.x = epi1(t.x, bf16_lo(bias.x), bf16_lo(res.x), w.x, d);
+    o.y = epi1(t.y, bf16_hi(bias.x), bf16_hi(res.x), w.y, d);
+    o.z = epi1(t.z, bf16_lo(bias.y), bf16_lo(res.y), w.z, d);
+    o.w = epi1(t.w, bf16_hi(bias.y), bf16_hi(res.y), w.w, d);
+    return o;
+}
+
+// ------------------------------------------------------------------ tile kernel
+template <int BK>
+struct TileCfg {
+    static constexpr int BM = kBM, BN = kBN;
+    static constexpr int NB = BN / 32;              // 32-column blocks per wave
+    static constexpr int KS = BK / 16;              // MFMA k steps per K step
+    static constexpr int LDK = BK + 8;              // padded LDS row (elements)
+    static constexpr int KB = BK / 8;               // 8-row groups of a W tile
+    static constexpr int NPT = BN * BK / (8 * kThreads);  // columns of a thread's W piece
+    static_assert(NPT == 2 || NPT == 4, "W piece is 8 k x 2 or 4 n");
+};
+
+template <int BK>
+__device__ __forceinline__ void load_x(uint4 (&x)[2][BK / 16], const uint16_t* const (&xrow)[2],
+                                       int64_t k) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s)
+            x[mb][s] = *reinterpret_cast<const uint4*>(xrow[mb] + k + 16 * s);
+}
+
+// A thread's piece of the W tile: 8 consecutive k rows x NPT consecutive n columns.
+template <int NPT>
+__device__ __forceinline__ void load_w(uint32_t (&w)[8][NPT / 2], const uint16_t* wcol, int64_t k,
+                                       int64_t N) {
+    const uint16_t* p = wcol + k * N;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if constexpr (NPT == 4) {
+            const uint2 v = *reinterpret_cast<const uint2*>(p + j * N);
+            w[j][0] = v.x;
+            w[j][1] = v.y;
+        } else {
+            w[j][0] = *reinterpret_cast<const uint32_t*>(p + j * N);
+        }
+    }
+}
+
+// Transpose the piece into NPT k-contiguous 16-byte rows of the LDS tile [BN][LDK].
+template <int NPT, int LDK>
+__device__ __forceinline__ void store_w(uint16_t* lds, const uint32_t (&w)[8][NPT / 2], int nq,
+                                        int kb) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+        uint32_t d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t a = w[2 * j][i / 2], b = w[2 * j + 1][i / 2];
+            d[j] = (i % 2 == 0) ? ((a & 0xFFFFu) | (b << 16)) : ((a >> 16) | (b & 0xFFFF0000u));
+        }
+        *reinterpret_cast<uint4*>(lds + (NPT * nq + i) * LDK + 8 * kb) =
+            make_uint4(d[0], d[1], d[2], d[3]);
+    }
+}
+
+template <int BK>
+__device__ __forceinline__ void mfma_step(f32x16 (&S)[kBN / 32][2], const uint16_t* lds,
+                                          const uint4 (&x)[2][BK / 16], int l32, int h) {
+    using C = TileCfg<BK>;
+#pragma unroll
+    for (int s = 0; s < C::KS; ++s) {
+        bf16x8 wf[C::NB];
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+            wf[nb] = *reinterpret_cast<const bf16x8*>(lds + (32 * nb + l32) * C::LDK + 16 * s + 8 * h);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    wf[nb], __builtin_bit_cast(bf16x8, x[mb][s]), S[nb][mb], 0, 0, 0);
+    }
+}
+
+template <int MODE, int BK>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void tile_kernel(TileArgs a) {
+    using C = TileCfg<BK>;
+    constexpr int BM = C::BM, BN = C::BN, NB = C::NB, LDK = C::LDK, NPT = C::NPT;
+    __shared__ __attribute__((aligned(16))) uint16_t lds[2][BN * LDK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, h = lane >> 5;
+
+    // XCD-aware slot: ids are dealt round-robin over 8 XCDs; give each XCD a contiguous
+    // run of items per sweep.
+    const int G = gridDim.x, bid = blockIdx.x;
+    const int slot = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+
+    const int tpcm = (a.cm + BM - 1) / BM, tpcn = (a.cn + BN - 1) / BN, tpc = tpcm * tpcn;
+    const int chunks_n = a.RN / a.cn;
+    const int n_tiles = (a.RM / a.cm) * chunks_n * tpc;
+
+    const int wkb = tid % C::KB, wnq = tid / C::KB;
+    const int sps = a.Ks / BK;   // K steps per slice
+
+    for (int item = slot; item < a.total_items; item += G) {
+        int tile_item = item, p_lo = 0, p_hi = a.P;
+        if (MODE == kModePartials) {
+            tile_item = item % n_tiles;
+            p_lo = item / n_tiles;
+            p_hi = p_lo + 1;
+        }
+        const int chunk = tile_item / tpc, t = tile_item - chunk * tpc;
+        const int cr = chunk / chunks_n, cc = chunk - cr * chunks_n;
+        constexpr int GM = 4;
+        const int first_tm = (t / (GM * tpcn)) * GM;
+        const int gm = min(GM, tpcm - first_tm);
+        const int tin = t - (t / (GM * tpcn)) * (GM * tpcn);
+        const int tm = first_tm + tin % gm, tn = tin / gm;
+        const int m0 = a.rm0 + cr * a.cm + tm * BM;
+        const int n0 = a.rn0 + cc * a.cn + tn * BN;
+        const int rows = min(BM, a.cm - tm * BM), cols = min(BN, a.cn - tn * BN);
+
+        const uint16_t* xrow[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int r = min(wave * 64 + mb * 32 + l32, rows - 1);
+            xrow[mb] = a.X + static_cast<int64_t>(m0 + r) * a.K + 8 * h;
+        }
+        const uint16_t* wcol =
+            a.W + static_cast<int64_t>(8 * wkb) * a.N + n0 + min(NPT * wnq, cols - NPT);
+
+        const int64_t k_first = static_cast<int64_t>(p_lo) * a.Ks;
+        const int64_t k_last = static_cast<int64_t>(p_hi) * a.Ks - BK;   // start of the last step
+
+        f32x16 S[NB][2], T[NB][2];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb) T[nb][mb] = f32x16{};
+        uint4 xc[2][C::KS], xn[2][C::KS];
+        uint32_t wr[8][NPT / 2];
+
+        load_x<BK>(xc, xrow, k_first);
+        load_w<NPT>(wr, wcol, k_first, a.N);
+        store_w<NPT, LDK>(lds[0], wr, wnq, wkb);
+        __syncthreads();
+
+        int buf = 0;
+        int64_t k = k_first;
+        for (int p = p_lo; p < p_hi; ++p) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) S[nb][mb] = f32x16{};
+            for (int j = 0; j < sps; ++j) {
+                // prefetch the next K step (the last step re-reads itself: no branch)
+                const int64_t kn = min(k + BK, k_last);
+                load_x<BK>(xn, xrow, kn);
+                load_w<NPT>(wr, wcol, kn, a.N);
+                mfma_step<BK>(S, lds[buf], xc, l32, h);
+                store_w<NPT, LDK>(lds[buf ^ 1], wr, wnq, wkb);
+                __syncthreads();
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int s = 0; s < C::KS; ++s) xc[mb][s] = xn[mb][s];
+                buf ^= 1;
+                k += BK;
+            }
+            // fixed-order fp32 slice reduction: T = 0 + S_0 (= S_0 exactly, an MFMA sum
+            // started from +0 is never -0), then T + S_1, T + S_2, ...
+            if (MODE != kModePartials) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) T[nb][mb] += S[nb][mb];
+            }
+        }
+
+        // Store / epilogue.  Lane holds rows m = 32 mb + l32 and, in registers 4g..4g+3
+        // of block nb, columns 32 nb + 8 g + 4 h + 0..3.
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int nl = 32 * nb + 8 * g + 4 * h;
+                if (nl >= cols) continue;
+                const int64_t n = n0 + nl;
+                uint2 bb = make_uint2(0u, 0u);
+                if (MODE == kModeFused) bb = *reinterpret_cast<const uint2*>(a.bias + n);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const int ml = wave * 64 + mb * 32 + l32;
+                    if (ml >= rows) continue;
+                    const int64_t m = m0 + ml;
+                    const f32x16& acc = (MODE == kModePartials) ? S[nb][mb] : T[nb][mb];
+                    const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
+                                                 acc[4 * g + 3]);
+                    if (MODE == kModeFused) {
+                        const int64_t e = m * a.N + n;
+                        const uint2 rb = *reinterpret_cast<const uint2*>(a.residual + e);
+                        *reinterpret_cast<float4*>(a.out + e) = epilogue4(v, bb, rb, e, a.drop);
+                    } else if (MODE == kModeReduced) {
+                        *reinterpret_cast<float4*>(a.out + m * a.N + n) = v;
+                    } else {
+                        float* dst = a.ws + static_cast<int64_t>(p_lo) * a.RM * a.RN +
+                                     (m - a.rm0) * a.RN + (n - a.rn0);
+                        *reinterpret_cast<float4*>(dst) = v;
+                    }
+                }
+            }
+    }
+}
+
+// ------------------------------------------------------------------ reduce + epilogue
+__global__ __launch_bounds__(256) void reduce_epilogue_kernel(ReduceArgs a) {
+    const int groups_per_row = a.RN / 4;
+    const int total = a.RM * groups_per_row;
+    const int64_t plane = static_cast<int64_t>(a.RM) * a.RN;
+    for (int q = blockIdx.x * 256 + threadIdx.x; q < total; q += gridDim.x * 256) {
+        const int r = q / groups_per_row, c = (q - r * groups_per_row) * 4;
+        const float* src = a.ws + static_cast<int64_t>(r) * a.RN + c;
+        float4 t = *reinterpret_cast<const float4*>(src);
+        for (int p = 1; p < a.P; ++p) {
+            const float4 s = *reinterpret_cast<const float4*>(src + p * plane);
+            t.x = __fadd_rn(t.x, s.x);
+            t.y = __fadd_rn(t.y, s.y);
+            t.z = __fadd_rn(t.z, s.z);
+            t.w = __fadd_rn(t.w, s.w);
+        }
+        const int64_t e = static_cast<int64_t>(a.rm0 + r) * a.N + (a.rn0 + c);
+        const uint2 bb = *reinterpret_cast<const uint2*>(a.bias + a.rn0 + c);
+        const uint2 rb = *reinterpret_cast<const uint2*>(a.residual + e);
+        *reinterpret_cast<float4*>(a.out + e) = epilogue4(t, bb, rb, e, a.drop);
+    }
+}
+
+// ------------------------------------------------------------------ fill (tuner inputs)
+__global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* p, int64_t n, uint32_t salt,
+                                                        float amp) {
+    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += gridDim.x * 256ll) {
+        uint32_t x = static_cast<uint32_t>(i) * 0x9E3779B1u ^ salt ^ static_cast<uint32_t>(i >> 32);
+        x ^= x >> 16;
+        x *= 0x7FEB352Du;
+        x ^= x >> 15;
+        x *= 0x846CA68Bu;
+        x ^= x >> 16;
+        const float u = __fmul_rn(static_cast<float>(x >> 8), 1.0f / 16777216.0f);  // [0, 1)
+        const float v = __fmul_rn(__fsub_rn(__fmul_rn(u, 2.0f), 1.0f), amp);
+        p[i] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
+    }
+}
+
+// ------------------------------------------------------------------ launchers
+template <int MODE, int BK>
+static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL((tile_kernel<MODE, BK>), dim3(grid), dim3(kThreads), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_tile(int mode, int bk, const TileArgs& a, int grid, hipStream_t s) {
+    if (bk == 64) {
+        if (mode == kModeFused) return launch_tile_t<kModeFused, 64>(a, grid, s);
+        if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64>(a, grid, s);
+        return launch_tile_t<kModePartials, 64>(a, grid, s);
+    }
+    if (mode == kModeFused) return launch_tile_t<kModeFused, 32>(a, grid, s);
+    if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32>(a, grid, s);
+    return launch_tile_t<kModePartials, 32>(a, grid, s);
+}
+
+hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s) {
+    hipLaunchKernelGGL(reduce_epilogue_kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s) {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(fill_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
+                       n, salt, amp);
+    return hipGetLastError();
+}
+
+template <int MODE, int BK>
+static int occ_t() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_kernel<MODE, BK>, kThreads, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
+int tile_occupancy(int mode, int bk) {
+    if (bk == 64) {
+        if (mode == kModeFused) return occ_t<kModeFused, 64>();
+        if (mode == kModeReduced) return occ_t<kModeReduced, 64>();
+        return occ_t<kModePartials, 64>();
+    }
+    if (mode == kModeFused) return occ_t<kModeFused, 32>();
+    if (mode == kModeReduced) return occ_t<kModeReduced, 32>();
+    return occ_t<kModePartials, 32>();
+}
+
+int reduce_occupancy() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_epilogue_kernel, 256, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
+}  // namespace mmar

@@ -1,0 +1,838 @@
+// Host side of the C ABI in include/mmar.h: argument checks, device checks, the chunk
+// scheduler (sequential, two-stream, persistent), the library workspace and the plan
+// cache / autotuner.
+//
+// The chunk scheduler is this library's form of the CoCoNet record's (LIT-735, "Key
+// takeaways", second bullet) overlap of the model-parallel MatMul with the AllReduce
+// that consumes it, "in chunks"; the autotuner is its "autotunes the schedule" (first
+// bullet).  The chunk-size trade-off it searches is the bucket-size one of the
+// overlap pages: small chunks pay per-launch latency, large ones leave the last chunk's
+// reduction exposed.
+#include "../../include/mmar.h"
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "mmar_internal.h"
+
+namespace {
+
+using mmar::DropParams;
+using mmar::ReduceArgs;
+using mmar::TileArgs;
+
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+    g_err = msg;
+    return code;
+}
+
+#define MMAR_HIP(call)                                                                     \
+    do {                                                                                   \
+        hipError_t e_ = (call);                                                            \
+        if (e_ != hipSuccess)                                                              \
+            return fail(MMAR_EHIP, std::string(#call) + ": " + hipGetErrorString(e_));     \
+    } while (0)
+
+struct Plan {
+    int sched = MMAR_SCHED_PERSISTENT;
+    int cm = 0, cn = 0, ring = 0;
+};
+
+constexpr int kMaxRing = 8;
+
+struct DevState {
+    int id = -1;
+    int cus = 0;
+    std::string arch;
+    int occ[3][2] = {};  // tile kernel occupancy per mode and (bk == 64 ? 0 : 1)
+    int red_occ = 0;
+    std::mutex mu;       // serializes use of the library workspace / side stream
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    hipStream_t side = nullptr;
+    hipEvent_t ev_entry = nullptr, ev_side_done = nullptr;
+    hipEvent_t ev_ws_free = nullptr;  // recorded after the last use of the library workspace
+    hipEvent_t ev_gemm[kMaxRing] = {}, ev_red[kMaxRing] = {};
+};
+
+std::mutex g_mu;  // guards g_dev and g_plans
+std::map<int, std::unique_ptr<DevState>> g_dev;
+using PlanKey = std::tuple<std::string, int64_t, int64_t, int64_t, int32_t>;
+std::map<PlanKey, Plan> g_plans;
+bool g_plans_loaded = false;
+
+// ------------------------------------------------------------------ validation
+struct Shape {
+    int64_t M, N, K;
+    int32_t P;
+};
+
+int check_shape(const Shape& s) {
+    if (s.M <= 0 || s.N <= 0 || s.K <= 0) return fail(MMAR_EINVAL, "M, N and K must be positive");
+    if (s.P < 1 || s.P > 4096) return fail(MMAR_EINVAL, "P must be in [1, 4096]");
+    if (s.K % s.P != 0) return fail(MMAR_EINVAL, "P must divide K");
+    if ((s.K / s.P) % 32 != 0) return fail(MMAR_EINVAL, "K/P must be a multiple of 32");
+    if (s.M % 32 != 0 || s.N % 32 != 0) return fail(MMAR_EINVAL, "M and N must be multiples of 32");
+    const int64_t lim = int64_t(1) << 31;
+    if (s.M >= lim || s.N >= lim || s.K >= lim || s.M * s.K >= lim || s.K * s.N >= lim ||
+        s.M * s.N >= lim)
+        return fail(MMAR_EINVAL, "every tensor must have fewer than 2^31 elements");
+    return MMAR_OK;
+}
+
+int check_chunk(const Shape& s, int32_t cm, int32_t cn) {
+    if (cm < 0 || cn < 0) return fail(MMAR_EINVAL, "chunk sizes must be >= 0");
+    if (cm != 0 && (cm % 32 != 0 || s.M % cm != 0))
+        return fail(MMAR_EINVAL, "chunk_m must be a multiple of 32 dividing M");
+    if (cn != 0 && (cn % 32 != 0 || s.N % cn != 0))
+        return fail(MMAR_EINVAL, "chunk_n must be a multiple of 32 dividing N");
+    return MMAR_OK;
+}
+
+int check_ptr(const void* p, const char* name) {
+    if (p == nullptr) return fail(MMAR_EINVAL, std::string(name) + " is NULL");
+    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
+        return fail(MMAR_EALIGN, std::string(name) + " is not 16-byte aligned");
+    return MMAR_OK;
+}
+
+int drop_params(float p, uint64_t seed, DropParams* d) {
+    if (!std::isfinite(p) || p < 0.0f || p > 1.0f)
+        return fail(MMAR_EINVAL, "p_drop must be finite and in [0, 1]");
+    const double pd = static_cast<double>(p);
+    d->key0 = static_cast<uint32_t>(seed);
+    d->key1 = static_cast<uint32_t>(seed >> 32);
+    if (p == 1.0f) {
+        d->drop_all = 1u;
+        d->thr = 0xFFFFFFFFu;
+        d->scale = 0.0f;
+    } else {
+        d->drop_all = 0u;
+        d->thr = static_cast<uint32_t>(std::floor(pd * 4294967296.0));  // < 2^32 for p < 1
+        d->scale = static_cast<float>(1.0 / (1.0 - pd));
+    }
+    return MMAR_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    const char* pa = static_cast<const char*>(a);
+    const char* pb = static_cast<const char*>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+// ------------------------------------------------------------------ devices
+int current_device(DevState** out) {
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return fail(MMAR_ENODEV, "no HIP device");
+    }
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(MMAR_ENODEV, "no current HIP device");
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_dev.find(dev);
+    if (it == g_dev.end()) {
+        auto st = std::make_unique<DevState>();
+        st->id = dev;
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+            return fail(MMAR_ENODEV, "hipGetDeviceProperties failed");
+        st->arch = prop.gcnArchName;
+        st->cus = prop.multiProcessorCount;
+        if (st->arch.compare(0, 6, "gfx950") == 0) {
+            for (int m = 0; m < 3; ++m) {
+                st->occ[m][0] = mmar::tile_occupancy(m, 64);
+                st->occ[m][1] = mmar::tile_occupancy(m, 32);
+            }
+            st->red_occ = mmar::reduce_occupancy();
+        }
+        it = g_dev.emplace(dev, std::move(st)).first;
+    }
+    DevState* st = it->second.get();
+    if (st->arch.compare(0, 6, "gfx950") != 0)
+        return fail(MMAR_ENODEV, "current device is " + st->arch + ", not gfx950");
+    *out = st;
+    return MMAR_OK;
+}
+
+int ensure_workspace(DevState* st, size_t bytes) {
+    if (st->ws_bytes >= bytes) return MMAR_OK;
+    if (st->ws) {
+        (void)hipDeviceSynchronize();
+        (void)hipFree(st->ws);
+        st->ws = nullptr;
+        st->ws_bytes = 0;
+    }
+    if (hipMalloc(&st->ws, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        st->ws = nullptr;
+        return fail(MMAR_ENOMEM, "workspace allocation of " + std::to_string(bytes) + " bytes failed");
+    }
+    st->ws_bytes = bytes;
+    return MMAR_OK;
+}
+
+int ensure_streams(DevState* st) {
+    if (st->side) return MMAR_OK;
+    MMAR_HIP(hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking));
+    MMAR_HIP(hipEventCreateWithFlags(&st->ev_entry, hipEventDisableTiming));
+    MMAR_HIP(hipEventCreateWithFlags(&st->ev_side_done, hipEventDisableTiming));
+    for (int i = 0; i < kMaxRing; ++i) {
+        MMAR_HIP(hipEventCreateWithFlags(&st->ev_gemm[i], hipEventDisableTiming));
+        MMAR_HIP(hipEventCreateWithFlags(&st->ev_red[i], hipEventDisableTiming));
+    }
+    MMAR_HIP(hipEventRecord(st->ev_side_done, st->side));
+    return MMAR_OK;
+}
+
+// ------------------------------------------------------------------ plans
+Plan default_plan(const Shape& s) {
+    Plan p;
+    p.sched = MMAR_SCHED_PERSISTENT;
+    p.cm = static_cast<int>(s.M);
+    p.cn = static_cast<int>(s.N);
+    p.ring = 0;
+    return p;
+}
+
+// Fill in zero chunk sizes / ring for a schedule.
+Plan resolve(const Shape& s, Plan p) {
+    if (p.sched == MMAR_SCHED_STREAMS) {
+        if (p.cm == 0) {
+            // about 8 chunks of whole rows by default, each a multiple of 256 rows if possible
+            int64_t cm = s.M;
+            for (int64_t c : {s.M / 8, s.M / 4, s.M / 2}) {
+                if (c >= 32 && c % 32 == 0 && s.M % c == 0) {
+                    cm = c;
+                    break;
+                }
+            }
+            p.cm = static_cast<int>(cm);
+        }
+        if (p.cn == 0) p.cn = static_cast<int>(s.N);
+        if (p.ring <= 0) p.ring = 2;
+        p.ring = std::min(p.ring, kMaxRing);
+    } else {
+        if (p.cm == 0) p.cm = static_cast<int>(s.M);
+        if (p.cn == 0) p.cn = static_cast<int>(s.N);
+        p.ring = p.sched == MMAR_SCHED_SEQUENTIAL ? 1 : 0;
+    }
+    return p;
+}
+
+size_t ws_bytes_for(const Shape& s, const Plan& p) {
+    const size_t slot = static_cast<size_t>(s.P) * static_cast<size_t>(p.cm) *
+                        static_cast<size_t>(p.cn) * sizeof(float);
+    if (p.sched == MMAR_SCHED_SEQUENTIAL) return slot;
+    if (p.sched == MMAR_SCHED_STREAMS) return slot * static_cast<size_t>(p.ring);
+    return 0;
+}
+
+void load_plan_cache_locked() {
+    if (g_plans_loaded) return;
+    g_plans_loaded = true;
+    const char* path = std::getenv("MMAR_PLAN_CACHE");
+    if (!path || !*path) return;
+    FILE* f = std::fopen(path, "r");
+    if (!f) return;
+    char line[512];
+    while (std::fgets(line, sizeof line, f)) {
+        char arch[64] = {0};
+        long long M, N, K;
+        int P, sched, cm, cn, ring;
+        if (std::sscanf(line,
+                        " {\"arch\": \"%63[^\"]\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
+                        "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d",
+                        arch, &M, &N, &K, &P, &sched, &cm, &cn, &ring) == 9) {
+            Plan p;
+            p.sched = sched;
+            p.cm = cm;
+            p.cn = cn;
+            p.ring = ring;
+            g_plans[PlanKey(arch, M, N, K, P)] = p;
+        }
+    }
+    std::fclose(f);
+}
+
+void save_plan_cache_locked() {
+    const char* path = std::getenv("MMAR_PLAN_CACHE");
+    if (!path || !*path) return;
+    FILE* f = std::fopen(path, "w");
+    if (!f) return;
+    std::fprintf(f, "[\n");
+    size_t i = 0;
+    for (const auto& kv : g_plans) {
+        const auto& k = kv.first;
+        const Plan& p = kv.second;
+        std::fprintf(f,
+                     " {\"arch\": \"%s\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
+                     "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d}%s\n",
+                     std::get<0>(k).c_str(), (long long)std::get<1>(k), (long long)std::get<2>(k),
+                     (long long)std::get<3>(k), std::get<4>(k), p.sched, p.cm, p.cn, p.ring,
+                     ++i < g_plans.size() ? "," : "");
+    }
+    std::fprintf(f, "]\n");
+    std::fclose(f);
+}
+
+Plan lookup_plan(const DevState* st, const Shape& s) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    load_plan_cache_locked();
+    auto it = g_plans.find(PlanKey(st->arch, s.M, s.N, s.K, s.P));
+    return it == g_plans.end() ? default_plan(s) : it->second;
+}
+
+// ------------------------------------------------------------------ runners
+struct Call {
+    const uint16_t *X, *W, *bias, *residual;
+    float* out;
+    Shape s;
+    DropParams drop;
+};
+
+int bk_for(const Shape& s) { return ((s.K / s.P) % 64 == 0) ? 64 : 32; }
+
+int grid_for(const DevState* st, int mode, int bk, int items) {
+    int occ = st->occ[mode][bk == 64 ? 0 : 1];
+    if (occ < 1) occ = 1;
+    const int resident = st->cus * occ;
+    return std::max(1, std::min(items, resident));
+}
+
+int tiles_in(int rows, int cols) {
+    return ((rows + mmar::kBM - 1) / mmar::kBM) * ((cols + mmar::kBN - 1) / mmar::kBN);
+}
+
+TileArgs tile_args(const Call& c, int rm0, int rn0, int RM, int RN, int cm, int cn) {
+    TileArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.X = c.X;
+    a.W = c.W;
+    a.bias = c.bias;
+    a.residual = c.residual;
+    a.out = c.out;
+    a.M = c.s.M;
+    a.N = c.s.N;
+    a.K = c.s.K;
+    a.P = c.s.P;
+    a.Ks = static_cast<int32_t>(c.s.K / c.s.P);
+    a.rm0 = rm0;
+    a.rn0 = rn0;
+    a.RM = RM;
+    a.RN = RN;
+    a.cm = cm;
+    a.cn = cn;
+    a.drop = c.drop;
+    return a;
+}
+
+int run_persistent(const DevState* st, const Call& c, int mode, int cm, int cn, hipStream_t s) {
+    const int bk = bk_for(c.s);
+    TileArgs a = tile_args(c, 0, 0, static_cast<int>(c.s.M), static_cast<int>(c.s.N), cm, cn);
+    const int64_t items =
+        static_cast<int64_t>(c.s.M / cm) * (c.s.N / cn) * tiles_in(cm, cn);
+    a.total_items = static_cast<int32_t>(items);
+    MMAR_HIP(mmar::launch_tile(mode, bk, a, grid_for(st, mode, bk, a.total_items), s));
+    return MMAR_OK;
+}
+
+int launch_partials(const DevState* st, const Call& c, int rm0, int rn0, int cm, int cn,
+                    float* ws, hipStream_t s) {
+    const int bk = bk_for(c.s);
+    TileArgs a = tile_args(c, rm0, rn0, cm, cn, cm, cn);
+    a.ws = ws;
+    const int64_t items = static_cast<int64_t>(tiles_in(cm, cn)) * c.s.P;
+    if (items >= (int64_t(1) << 31)) return fail(MMAR_EINVAL, "too many work items");
+    a.total_items = static_cast<int32_t>(items);
+    MMAR_HIP(mmar::launch_tile(mmar::kModePartials, bk, a,
+                               grid_for(st, mmar::kModePartials, bk, a.total_items), s));
+    return MMAR_OK;
+}
+
+int launch_reduce(const DevState* st, const float* ws, const uint16_t* bias,
+                  const uint16_t* residual, float* out, int64_t N, int P, int rm0, int rn0,
+                  int RM, int RN, const DropParams& d, hipStream_t s) {
+    ReduceArgs r;
+    r.ws = ws;
+    r.bias = bias;
+    r.residual = residual;
+    r.out = out;
+    r.N = N;
+    r.P = P;
+    r.rm0 = rm0;
+    r.rn0 = rn0;
+    r.RM = RM;
+    r.RN = RN;
+    r.drop = d;
+    const int64_t groups = static_cast<int64_t>(RM) * (RN / 4);
+    int occ = std::max(1, st->red_occ);
+    int64_t grid = std::min<int64_t>((groups + 255) / 256, static_cast<int64_t>(st->cus) * occ * 2);
+    MMAR_HIP(mmar::launch_reduce_epilogue(r, static_cast<int>(std::max<int64_t>(1, grid)), s));
+    return MMAR_OK;
+}
+
+// Sequential (ring == 1, one stream) or two-stream chunk pipeline.
+int run_chunked(DevState* st, const Call& c, const Plan& p, float* ws, hipStream_t s) {
+    const int cm = p.cm, cn = p.cn;
+    const int chunks_m = static_cast<int>(c.s.M / cm), chunks_n = static_cast<int>(c.s.N / cn);
+    const size_t slot_elems = static_cast<size_t>(c.s.P) * cm * cn;
+    const bool two = p.sched == MMAR_SCHED_STREAMS;
+    const int ring = two ? p.ring : 1;
+    if (two) {
+        int rc = ensure_streams(st);
+        if (rc) return rc;
+        // earlier reductions on the side stream must be done before slots are rewritten
+        MMAR_HIP(hipStreamWaitEvent(s, st->ev_side_done, 0));
+    }
+    int last_slot = 0;
+    for (int ch = 0; ch < chunks_m * chunks_n; ++ch) {
+        const int cr = ch / chunks_n, cc = ch % chunks_n;
+        const int slot = ch % ring;
+        float* w = ws + slot * slot_elems;
+        if (two && ch >= ring) MMAR_HIP(hipStreamWaitEvent(s, st->ev_red[slot], 0));
+        int rc = launch_partials(st, c, cr * cm, cc * cn, cm, cn, w, s);
+        if (rc) return rc;
+        if (two) {
+            MMAR_HIP(hipEventRecord(st->ev_gemm[slot], s));
+            MMAR_HIP(hipStreamWaitEvent(st->side, st->ev_gemm[slot], 0));
+            rc = launch_reduce(st, w, c.bias, c.residual, c.out, c.s.N, c.s.P, cr * cm, cc * cn,
+                               cm, cn, c.drop, st->side);
+            if (rc) return rc;
+            MMAR_HIP(hipEventRecord(st->ev_red[slot], st->side));
+        } else {
+            rc = launch_reduce(st, w, c.bias, c.residual, c.out, c.s.N, c.s.P, cr * cm, cc * cn,
+                               cm, cn, c.drop, s);
+            if (rc) return rc;
+        }
+        last_slot = slot;
+    }
+    if (two) {
+        MMAR_HIP(hipEventRecord(st->ev_side_done, st->side));
+        MMAR_HIP(hipStreamWaitEvent(s, st->ev_red[last_slot], 0));
+    }
+    return MMAR_OK;
+}
+
+int run_plan(DevState* st, const Call& c, const Plan& p, void* workspace, size_t ws_bytes,
+             hipStream_t s) {
+    if (p.sched == MMAR_SCHED_PERSISTENT)
+        return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s);
+    const size_t need = ws_bytes_for(c.s, p);
+    if (workspace) {
+        if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+            return fail(MMAR_EALIGN, "workspace is not 16-byte aligned");
+        if (ws_bytes < need)
+            return fail(MMAR_ENOMEM, "workspace too small: need " + std::to_string(need) + " bytes");
+        return run_chunked(st, c, p, static_cast<float*>(workspace), s);
+    }
+    std::lock_guard<std::mutex> lk(st->mu);
+    int rc = ensure_workspace(st, need);
+    if (rc) return rc;
+    if (!st->ev_ws_free) MMAR_HIP(hipEventCreateWithFlags(&st->ev_ws_free, hipEventDisableTiming));
+    else MMAR_HIP(hipStreamWaitEvent(s, st->ev_ws_free, 0));  // an earlier call on another stream
+    rc = run_chunked(st, c, p, static_cast<float*>(st->ws), s);
+    if (rc) return rc;
+    MMAR_HIP(hipEventRecord(st->ev_ws_free, s));
+    return MMAR_OK;
+}
+
+int check_call(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+               const uint16_t* residual, float* out, const Shape& s, float p_drop,
+               uint64_t seed, int32_t cm, int32_t cn, Call* c) {
+    int rc;
+    if ((rc = check_shape(s))) return rc;
+    if ((rc = check_chunk(s, cm, cn))) return rc;
+    if ((rc = check_ptr(X, "X"))) return rc;
+    if ((rc = check_ptr(W, "W"))) return rc;
+    if ((rc = check_ptr(bias, "bias"))) return rc;
+    if ((rc = check_ptr(residual, "residual"))) return rc;
+    if ((rc = check_ptr(out, "out"))) return rc;
+    const size_t ob = static_cast<size_t>(s.M * s.N) * 4;
+    if (overlaps(out, ob, X, static_cast<size_t>(s.M * s.K) * 2) ||
+        overlaps(out, ob, W, static_cast<size_t>(s.K * s.N) * 2) ||
+        overlaps(out, ob, bias, static_cast<size_t>(s.N) * 2) ||
+        overlaps(out, ob, residual, static_cast<size_t>(s.M * s.N) * 2))
+        return fail(MMAR_EINVAL, "out overlaps an input");
+    if ((rc = drop_params(p_drop, seed, &c->drop))) return rc;
+    c->X = X;
+    c->W = W;
+    c->bias = bias;
+    c->residual = residual;
+    c->out = out;
+    c->s = s;
+    return MMAR_OK;
+}
+
+int fused_impl(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+               const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+               int32_t P, float p_drop, uint64_t seed, int32_t sched, int32_t chunk_m,
+               int32_t chunk_n, int32_t ring, void* workspace, size_t ws_bytes,
+               void* stream) {
+    g_err.clear();
+    Call c;
+    const Shape s{M, N, K, P};
+    int rc = check_call(X, W, bias, residual, out, s, p_drop, seed, chunk_m, chunk_n, &c);
+    if (rc) return rc;
+    if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_PERSISTENT)
+        return fail(MMAR_EINVAL, "unknown schedule");
+    if (ring < 0 || ring > kMaxRing) return fail(MMAR_EINVAL, "ring must be in [0, 8]");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    Plan p;
+    if (sched == MMAR_SCHED_AUTO) {
+        p = lookup_plan(st, s);
+    } else {
+        p.sched = sched;
+        p.ring = ring;
+    }
+    if (chunk_m) p.cm = chunk_m;
+    if (chunk_n) p.cn = chunk_n;
+    if (sched != MMAR_SCHED_AUTO && ring) p.ring = ring;
+    p = resolve(s, p);
+    return run_plan(st, c, p, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------------------ autotuner
+int time_plan(DevState* st, const Call& c, const Plan& p, hipStream_t s, float* ms_out) {
+    hipEvent_t e0, e1;
+    MMAR_HIP(hipEventCreate(&e0));
+    MMAR_HIP(hipEventCreate(&e1));
+    int rc = MMAR_OK;
+    for (int i = 0; i < 2 && !rc; ++i) rc = run_plan(st, c, p, nullptr, 0, s);
+    std::vector<float> t;
+    for (int i = 0; i < 5 && !rc; ++i) {
+        if (hipEventRecord(e0, s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
+        if (!rc) rc = run_plan(st, c, p, nullptr, 0, s);
+        if (!rc && hipEventRecord(e1, s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
+        if (!rc && hipEventSynchronize(e1) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventSynchronize");
+        float ms = 0;
+        if (!rc && hipEventElapsedTime(&ms, e0, e1) != hipSuccess) rc = fail(MMAR_EHIP, "elapsed");
+        t.push_back(ms);
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (rc) return rc;
+    std::sort(t.begin(), t.end());
+    *ms_out = t[t.size() / 2];
+    return MMAR_OK;
+}
+
+std::vector<int> divisors32(int64_t n, std::initializer_list<int> parts) {
+    std::vector<int> out;
+    for (int d : parts) {
+        if (n % d) continue;
+        const int64_t c = n / d;
+        if (c % 32 == 0 && std::find(out.begin(), out.end(), static_cast<int>(c)) == out.end())
+            out.push_back(static_cast<int>(c));
+    }
+    return out;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+int mmar_fused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+               const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+               int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
+               void* stream) {
+    return fused_impl(X, W, bias, residual, out, M, N, K, P, p_drop, seed, MMAR_SCHED_AUTO,
+                      chunk_m, chunk_n, 0, nullptr, 0, stream);
+}
+
+size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, int32_t P,
+                            int32_t chunk_m, int32_t chunk_n, int32_t ring) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    if (check_shape(s) || check_chunk(s, chunk_m, chunk_n)) return 0;
+    if (schedule < MMAR_SCHED_AUTO || schedule > MMAR_SCHED_PERSISTENT || ring < 0 ||
+        ring > kMaxRing) {
+        fail(MMAR_EINVAL, "bad schedule or ring");
+        return 0;
+    }
+    Plan p;
+    if (schedule == MMAR_SCHED_AUTO) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        load_plan_cache_locked();
+        int dev = -1;
+        std::string arch = "gfx950";
+        if (hipGetDevice(&dev) == hipSuccess) {
+            auto it = g_dev.find(dev);
+            if (it != g_dev.end()) arch = it->second->arch;
+        } else {
+            (void)hipGetLastError();
+        }
+        auto pit = g_plans.find(PlanKey(arch, M, N, K, P));
+        p = pit == g_plans.end() ? default_plan(s) : pit->second;
+    } else {
+        p.sched = schedule;
+        p.ring = ring;
+    }
+    if (chunk_m) p.cm = chunk_m;
+    if (chunk_n) p.cn = chunk_n;
+    if (schedule != MMAR_SCHED_AUTO && ring) p.ring = ring;
+    return ws_bytes_for(s, resolve(s, p));
+}
+
+int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                  const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                  int32_t P, float p_drop, uint64_t seed, int32_t schedule, int32_t chunk_m,
+                  int32_t chunk_n, int32_t ring, void* workspace, size_t ws_bytes,
+                  void* stream) {
+    return fused_impl(X, W, bias, residual, out, M, N, K, P, p_drop, seed, schedule, chunk_m,
+                      chunk_n, ring, workspace, ws_bytes, stream);
+}
+
+int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                    const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                    int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
+                    void* stream) {
+    return fused_impl(X, W, bias, residual, out, M, N, K, P, p_drop, seed,
+                      MMAR_SCHED_SEQUENTIAL, chunk_m, chunk_n, 0, nullptr, 0, stream);
+}
+
+int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M, int64_t N,
+                   int64_t K, int32_t P, int32_t chunk_m, int32_t chunk_n, void* stream) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    int rc;
+    if ((rc = check_shape(s)) || (rc = check_chunk(s, chunk_m, chunk_n))) return rc;
+    if ((rc = check_ptr(X, "X")) || (rc = check_ptr(W, "W")) || (rc = check_ptr(T_out, "T_out")))
+        return rc;
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    Call c;
+    std::memset(&c, 0, sizeof c);
+    c.X = X;
+    c.W = W;
+    c.out = T_out;
+    c.s = s;
+    return run_persistent(st, c, mmar::kModeReduced, chunk_m ? chunk_m : static_cast<int>(M),
+                          chunk_n ? chunk_n : static_cast<int>(N),
+                          static_cast<hipStream_t>(stream));
+}
+
+int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, int64_t M,
+                       int64_t N, int64_t K, int32_t P, void* stream) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    int rc;
+    if ((rc = check_shape(s))) return rc;
+    if ((rc = check_ptr(X, "X")) || (rc = check_ptr(W, "W")) ||
+        (rc = check_ptr(partials, "partials")))
+        return rc;
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    Call c;
+    std::memset(&c, 0, sizeof c);
+    c.X = X;
+    c.W = W;
+    c.s = s;
+    return launch_partials(st, c, 0, 0, static_cast<int>(M), static_cast<int>(N), partials,
+                           static_cast<hipStream_t>(stream));
+}
+
+int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
+                              const uint16_t* residual, float* out, int64_t M, int64_t N,
+                              int32_t P, float p_drop, uint64_t seed, void* stream) {
+    g_err.clear();
+    int rc;
+    if (M <= 0 || N <= 0 || M % 32 || N % 32 || P < 1 || P > 4096 || M * N >= (int64_t(1) << 31))
+        return fail(MMAR_EINVAL, "bad M, N or P (M, N positive multiples of 32; 1 <= P <= 4096)");
+    if ((rc = check_ptr(partials, "partials")) || (rc = check_ptr(bias, "bias")) ||
+        (rc = check_ptr(residual, "residual")) || (rc = check_ptr(out, "out")))
+        return rc;
+    DropParams d;
+    if ((rc = drop_params(p_drop, seed, &d))) return rc;
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    return launch_reduce(st, partials, bias, residual, out, N, P, 0, 0, static_cast<int>(M),
+                         static_cast<int>(N), d, static_cast<hipStream_t>(stream));
+}
+
+int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
+                  int32_t chunk_m, int32_t chunk_n, int32_t ring) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    int rc;
+    if ((rc = check_shape(s)) || (rc = check_chunk(s, chunk_m, chunk_n))) return rc;
+    if (schedule < MMAR_SCHED_AUTO || schedule > MMAR_SCHED_PERSISTENT || ring < 0 ||
+        ring > kMaxRing)
+        return fail(MMAR_EINVAL, "bad schedule or ring");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    std::lock_guard<std::mutex> lk(g_mu);
+    load_plan_cache_locked();
+    const PlanKey key(st->arch, M, N, K, P);
+    if (schedule == MMAR_SCHED_AUTO) {
+        g_plans.erase(key);
+        return MMAR_OK;
+    }
+    Plan p;
+    p.sched = schedule;
+    p.cm = chunk_m;
+    p.cn = chunk_n;
+    p.ring = ring;
+    g_plans[key] = resolve(s, p);
+    return MMAR_OK;
+}
+
+int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
+                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    int rc;
+    if ((rc = check_shape(s))) return rc;
+    if (!schedule || !chunk_m || !chunk_n || !ring) return fail(MMAR_EINVAL, "NULL output pointer");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    const Plan p = resolve(s, lookup_plan(st, s));
+    *schedule = p.sched;
+    *chunk_m = p.cm;
+    *chunk_n = p.cn;
+    *ring = p.ring;
+    return MMAR_OK;
+}
+
+int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    int rc;
+    if ((rc = check_shape(s))) return rc;
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+
+    // candidate plans
+    std::vector<Plan> cands;
+    for (int cm : divisors32(M, {1, 2, 4}))
+        for (int cn : divisors32(N, {1, 2})) {
+            Plan p;
+            p.sched = MMAR_SCHED_PERSISTENT;
+            p.cm = cm;
+            p.cn = cn;
+            cands.push_back(p);
+        }
+    if (flags & 1u) {
+        for (int cm : divisors32(M, {2, 4, 8, 16}))
+            for (int r : {2, 3}) {
+                Plan p;
+                p.sched = MMAR_SCHED_STREAMS;
+                p.cm = cm;
+                p.cn = static_cast<int>(N);
+                p.ring = r;
+                cands.push_back(p);
+            }
+        Plan p;
+        p.sched = MMAR_SCHED_SEQUENTIAL;
+        cands.push_back(p);
+    }
+
+    // library-owned inputs with the value spread of the block's inputs
+    uint16_t *X = nullptr, *W = nullptr, *b = nullptr, *r = nullptr;
+    float* o = nullptr;
+    hipStream_t stream = nullptr;
+    auto cleanup = [&]() {
+        if (stream) (void)hipStreamSynchronize(stream);
+        (void)hipFree(X);
+        (void)hipFree(W);
+        (void)hipFree(b);
+        (void)hipFree(r);
+        (void)hipFree(o);
+        if (stream) (void)hipStreamDestroy(stream);
+    };
+    if (hipMalloc(&X, M * K * 2) != hipSuccess || hipMalloc(&W, K * N * 2) != hipSuccess ||
+        hipMalloc(&b, N * 2) != hipSuccess || hipMalloc(&r, M * N * 2) != hipSuccess ||
+        hipMalloc(&o, M * N * 4) != hipSuccess || hipStreamCreate(&stream) != hipSuccess) {
+        (void)hipGetLastError();
+        cleanup();
+        return fail(MMAR_ENOMEM, "autotune buffers");
+    }
+    if (mmar::launch_fill_bf16(X, M * K, 1u, 2.0f, stream) != hipSuccess ||
+        mmar::launch_fill_bf16(W, K * N, 2u, 0.04f, stream) != hipSuccess ||
+        mmar::launch_fill_bf16(b, N, 3u, 0.04f, stream) != hipSuccess ||
+        mmar::launch_fill_bf16(r, M * N, 4u, 2.0f, stream) != hipSuccess) {
+        cleanup();
+        return fail(MMAR_EHIP, "autotune fill");
+    }
+    Call c;
+    c.X = X;
+    c.W = W;
+    c.bias = b;
+    c.residual = r;
+    c.out = o;
+    c.s = s;
+    drop_params(0.1f, 1234, &c.drop);
+
+    Plan best;
+    float best_ms = 1e30f;
+    for (Plan p : cands) {
+        p = resolve(s, p);
+        float ms = 0;
+        rc = time_plan(st, c, p, stream, &ms);
+        if (rc) {
+            cleanup();
+            return rc;
+        }
+        if (ms < best_ms) {
+            best_ms = ms;
+            best = p;
+        }
+    }
+    cleanup();
+    std::lock_guard<std::mutex> lk(g_mu);
+    load_plan_cache_locked();
+    g_plans[PlanKey(st->arch, M, N, K, P)] = best;
+    save_plan_cache_locked();
+    return MMAR_OK;
+}
+
+const char* mmar_last_error(void) { return g_err.c_str(); }
+
+const char* mmar_version(void) { return "mmar 0.1.0 gfx950"; }
+
+int mmar_release(void) {
+    g_err.clear();
+    std::lock_guard<std::mutex> lk(g_mu);
+    int cur = -1;
+    const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+    for (auto& kv : g_dev) {
+        DevState* st = kv.second.get();
+        std::lock_guard<std::mutex> dl(st->mu);
+        if (hipSetDevice(st->id) != hipSuccess) continue;
+        (void)hipDeviceSynchronize();
+        if (st->ws) (void)hipFree(st->ws);
+        st->ws = nullptr;
+        if (st->ev_ws_free) (void)hipEventDestroy(st->ev_ws_free);
+        st->ev_ws_free = nullptr;
+        st->ws_bytes = 0;
+        if (st->side) {
+            (void)hipStreamDestroy(st->side);
+            st->side = nullptr;
+            (void)hipEventDestroy(st->ev_entry);
+            (void)hipEventDestroy(st->ev_side_done);
+            for (int i = 0; i < kMaxRing; ++i) {
+                (void)hipEventDestroy(st->ev_gemm[i]);
+                (void)hipEventDestroy(st->ev_red[i]);
+            }
+        }
+    }
+    if (have_cur) (void)hipSetDevice(cur);
+    (void)hipGetLastError();
+    return MMAR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// Internal interface between the host scheduler (mmar.cpp) and the gfx950 kernels
+// (kernels.hip).  Not installed; the public interface is include/mmar.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mmar {
+
+// What the tile kernel does with each finished output tile.
+enum TileMode : int {
+    kModeFused = 0,     // all P slices, reduced in registers, then bias/dropout/residual
+    kModeReduced = 1,   // all P slices, reduced in registers, stored as fp32 T
+    kModePartials = 2,  // one slice per work item, stored as fp32 S_p to a workspace
+};
+
+// Dropout parameters as the kernels use them.
+struct DropParams {
+    uint32_t thr;       // drop iff Philox word < thr
+    uint32_t drop_all;  // p == 1: every element is dropped
+    float scale;        // fp32(1 / (1 - p)); 1 when p == 0
+    uint32_t key0, key1;
+};
+
+// Arguments of the tile kernel.  The kernel covers the output region
+// [rm0, rm0 + RM) x [rn0, rn0 + RN), split into chunks of cm x cn (which divide RM and
+// RN) and each chunk into BM x BN tiles visited in chunk order.
+struct TileArgs {
+    const uint16_t* X;   // [M, K] bf16 bits
+    const uint16_t* W;   // [K, N] bf16 bits
+    const uint16_t* bias;
+    const uint16_t* residual;
+    float* out;          // kModeFused / kModeReduced: [M, N]
+    float* ws;           // kModePartials: [P][RM][RN] for the region
+    int64_t M, N, K;
+    int32_t P, Ks;       // Ks = K / P
+    int32_t rm0, rn0, RM, RN;
+    int32_t cm, cn;
+    int32_t total_items; // tiles (x P for kModePartials)
+    DropParams drop;
+};
+
+struct ReduceArgs {
+    const float* ws;     // [P][RM][RN]
+    const uint16_t* bias;
+    const uint16_t* residual;
+    float* out;          // [M, N]
+    int64_t N;           // leading dimension of out / residual
+    int32_t P;
+    int32_t rm0, rn0, RM, RN;
+    DropParams drop;
+};
+
+constexpr int kBM = 256;   // output rows per tile (4 waves x 64)
+constexpr int kBN = 128;   // output columns per tile
+constexpr int kThreads = 256;
+
+// Launchers (kernels.hip).  bk is 64 or 32 (the K step; it must divide Ks).
+hipError_t launch_tile(int mode, int bk, const TileArgs& a, int grid, hipStream_t s);
+hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s);
+hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s);
+// Workgroups of the tile kernel that fit on one CU at once (0 on error).
+int tile_occupancy(int mode, int bk);
+int reduce_occupancy();
+
+}  // namespace mmar

@@ -1,0 +1,169 @@
+/*
+ * mmar.h -- C ABI of the fused MatMul -> slice-reduce -> epilogue library (gfx950).
+ *
+ * The block.  A row-parallel (tensor-parallel) linear layer splits its contraction over
+ * P ranks; rank p computes the partial product S_p = X[:, K_p] . W[K_p, :] and an
+ * AllReduce sums the partials (CoCoNet record LIT-735, "Key takeaways", second bullet:
+ * the model-parallel MatMul followed by the AllReduce that consumes it, overlapped in
+ * chunks).  The pointwise work after it is fused into the reduction (same page, first
+ * bullet: fusing pointwise work into a collective).  This library folds the P ranks
+ * onto one GPU as P K-slices and computes
+ *
+ *     out = residual + dropout_p( bias + sum_{p=0}^{P-1} X[:, K_p] . W[K_p, :] )
+ *
+ * with K_p = [p*K/P, (p+1)*K/P).  Each partial S_p is accumulated in fp32 from zero;
+ * the partials are added in fp32 in the fixed order p = 0, 1, ..., P-1 starting from
+ * S_0, output chunk by output chunk; then v = T + bias[n], kept elements become
+ * residual + v * scale and dropped ones residual, with scale = fp32(1 / (1 - p)).  The
+ * keep decision is counter-based (Philox4x32-10, Salmon et al., SC'11): for the
+ * element at row m, column n, e = m*N + n, the block with counter
+ * (lo32(e>>2), hi32(e>>2), 0, 0) and key (lo32(seed), hi32(seed)) gives word
+ * r = block[e & 3]; the element is dropped iff r < floor(p * 2^32).  The mask therefore
+ * does not depend on chunking or on the schedule, and neither do the output bits:
+ * every schedule below produces identical bytes.
+ *
+ * Schedules (the chunk scheduler; the page's "overlapping the two in chunks"):
+ *   MMAR_SCHED_SEQUENTIAL  GEMM of a chunk's P partials into a workspace, then the
+ *                          reduce+epilogue of that chunk, on one stream, no overlap.
+ *   MMAR_SCHED_STREAMS     the same two kernels, the reduce+epilogue of chunk c on a
+ *                          second HIP stream while the GEMM of chunk c+1 runs; a ring
+ *                          of R workspace slots.
+ *   MMAR_SCHED_PERSISTENT  one persistent kernel: each workgroup walks output tiles in
+ *                          chunk order, reduces the P slices of a tile in registers and
+ *                          applies the epilogue before moving on; no partials reach HBM.
+ *
+ * Layouts.  X [M,K], W [K,N], residual [M,N] row-major, contiguous, bf16 bit patterns
+ * (uint16); bias [N] bf16 bits; out [M,N] row-major fp32.  All tensor pointers are
+ * DEVICE pointers on the current HIP device.
+ *
+ * Preconditions (checked; violations return MMAR_EINVAL before any device work and
+ * leave `out` untouched): M, N, K > 0; 1 <= P <= 4096; K % P == 0; (K/P) % 32 == 0;
+ * M % 32 == 0; N % 32 == 0; every tensor has fewer than 2^31 elements; p_drop finite
+ * and in [0, 1]; chunk_m / chunk_n each 0 (library choice) or a multiple of 32 dividing
+ * M (resp. N).  Pointers must be 16-byte aligned (else MMAR_EALIGN).  `out` must not
+ * overlap any input.
+ *
+ * Ownership.  The caller owns every tensor and keeps it alive until the stream has
+ * passed the call; the library never frees or retains caller memory.  The library owns
+ * a per-device workspace, a second stream and events, created on first use and freed by
+ * mmar_release().  Calls that use the library workspace are serialized per device by a
+ * mutex; with a caller workspace (mmar_fused_ex) calls are re-entrant.
+ *
+ * Errors.  Every int-returning call returns MMAR_OK (0) or a negative code; details of
+ * the last failure on the calling thread are in mmar_last_error().  Asynchronous device
+ * faults surface at the caller's next synchronization, as for any HIP kernel.  No C++
+ * exception crosses this interface.
+ *
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default stream).  All
+ * work is ordered after earlier work on `stream` and before later work on it: the
+ * second stream of MMAR_SCHED_STREAMS waits for `stream` on entry and `stream` waits
+ * for it before the call returns.
+ */
+#ifndef MMAR_H
+#define MMAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MMAR_OK = 0,
+    MMAR_EINVAL = -1, /* bad argument; nothing was launched */
+    MMAR_EALIGN = -2, /* a pointer is not 16-byte aligned */
+    MMAR_ENODEV = -3, /* no gfx950 device is current */
+    MMAR_ENOMEM = -4, /* device allocation failed or workspace too small */
+    MMAR_EHIP = -5    /* a HIP runtime call failed; see mmar_last_error() */
+};
+
+enum {
+    MMAR_SCHED_AUTO = 0,
+    MMAR_SCHED_SEQUENTIAL = 1,
+    MMAR_SCHED_STREAMS = 2,
+    MMAR_SCHED_PERSISTENT = 3
+};
+
+/* The fused block with the library's schedule for this shape: the plan set by
+ * mmar_set_plan or found by mmar_autotune, else the persistent schedule.  chunk_m /
+ * chunk_n override the plan's chunk when non-zero.  Uses the library workspace. */
+int mmar_fused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+               const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+               int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
+               void* stream);
+
+/* Workspace bytes a schedule needs (0 for MMAR_SCHED_PERSISTENT; for AUTO, the plan's).
+ * ring = number of chunk slots for MMAR_SCHED_STREAMS (0 = the default, 2).
+ * Returns 0 and sets the last error on invalid sizes. */
+size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, int32_t P,
+                            int32_t chunk_m, int32_t chunk_n, int32_t ring);
+
+/* The fused block with every choice explicit.  workspace == NULL: the library's
+ * workspace is used (serialized per device); otherwise `workspace` (device memory,
+ * 16-byte aligned, at least mmar_workspace_bytes(...) bytes, owned by the caller and not
+ * used by any other call until the stream passes this one) and the call is re-entrant.
+ * A too-small caller workspace returns MMAR_ENOMEM. */
+int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                  const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                  int32_t P, float p_drop, uint64_t seed, int32_t schedule, int32_t chunk_m,
+                  int32_t chunk_n, int32_t ring, void* workspace, size_t ws_bytes,
+                  void* stream);
+
+/* MMAR_SCHED_SEQUENTIAL with the library workspace: the "same fusion without overlap"
+ * comparison point of the CoCoNet record ("Key takeaways", second bullet). */
+int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                    const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                    int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
+                    void* stream);
+
+/* Measurement entry point: the persistent kernel with the epilogue removed.  Writes the
+ * reduced sum T = S_0 + ... + S_{P-1} (fp32, fixed order) to T_out [M,N]; the same
+ * MFMA sequence as mmar_fused, so T_out + epilogue reproduces its bits. */
+int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M, int64_t N,
+                   int64_t K, int32_t P, int32_t chunk_m, int32_t chunk_n, void* stream);
+
+/* Measurement entry point: the P per-slice partials S_p, fp32, written to
+ * partials [P][M][N] (each slice accumulated from zero). */
+int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, int64_t M,
+                       int64_t N, int64_t K, int32_t P, void* stream);
+
+/* The slice reduction plus epilogue alone, over P materialized fp32 partials
+ * [P][M][N]: T = S_0 + S_1 + ... (fixed order), then the bias, dropout and residual
+ * epilogue.  With P = 1 it is the epilogue alone over a materialized T. */
+int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
+                              const uint16_t* residual, float* out, int64_t M, int64_t N,
+                              int32_t P, float p_drop, uint64_t seed, void* stream);
+
+/* The autotuner (the page's "autotunes the schedule", "Key takeaways", first bullet):
+ * times candidate {schedule, chunk, ring} plans for this shape on library-owned
+ * buffers, keeps the fastest in the plan cache (also written to the JSON file named by
+ * the MMAR_PLAN_CACHE environment variable, if set) and returns MMAR_OK.  flags: bit 0
+ * = also try MMAR_SCHED_STREAMS and MMAR_SCHED_SEQUENTIAL plans.  Synchronizes the
+ * device. */
+int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags);
+
+/* Set / read the plan used by mmar_fused for this shape on the current device.
+ * schedule is one of MMAR_SCHED_*, AUTO clears the entry.  mmar_get_plan writes the
+ * plan that mmar_fused would use (the default when none is set). */
+int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
+                  int32_t chunk_m, int32_t chunk_n, int32_t ring);
+int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
+                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring);
+
+/* Text of the last error on the calling thread ("" if none).  Valid until the next
+ * call on this thread. */
+const char* mmar_last_error(void);
+
+/* Library version string, e.g. "mmar 0.1.0 gfx950". */
+const char* mmar_version(void);
+
+/* Frees the library's workspaces, streams and events on every device.  Synchronizes
+ * the devices first.  Safe to call more than once. */
+int mmar_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MMAR_H */

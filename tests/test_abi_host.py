@@ -1,0 +1,82 @@
+"""Host-side checks of the C ABI: the library loads, exports what include/mmar.h
+declares, and rejects bad arguments before touching any device."""
+import ctypes
+
+import pytest
+
+import chunked_matmul_reduce_amd as mmar
+
+FAKE = 1 << 20          # 16-byte aligned stand-in pointer; never reaches a device
+
+
+def _fused(**kw):
+    a = dict(X=FAKE, W=FAKE * 2, bias=FAKE * 3, res=FAKE * 4, out=FAKE * 64, M=64, N=256, K=256, P=4,
+             p=0.1, seed=0, cm=0, cn=0)
+    a.update(kw)
+    return mmar.lib.mmar_fused(a["X"], a["W"], a["bias"], a["res"], a["out"], a["M"], a["N"], a["K"],
+                               a["P"], a["p"], a["seed"], a["cm"], a["cn"], None)
+
+
+def test_every_declared_function_is_exported():
+    names = mmar.header_functions()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(mmar.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(mmar._SIGNATURES)
+
+
+def test_version():
+    assert mmar.version().startswith("mmar ") and "gfx950" in mmar.version()
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(X=None), "X is NULL"), (dict(out=None), "out is NULL"),
+    (dict(M=0), "positive"), (dict(P=3), "P must divide K"), (dict(K=96, P=2), "multiple of 32"),
+    (dict(M=48), "multiples of 32"), (dict(N=40), "multiples of 32"), (dict(P=0), "P must be"),
+    (dict(p=-0.1), "p_drop"), (dict(p=1.01), "p_drop"), (dict(p=float("nan")), "p_drop"),
+    (dict(p=float("inf")), "p_drop"), (dict(cm=48), "chunk_m"), (dict(cn=100), "chunk_n"),
+    (dict(cm=-32), "chunk"), (dict(out=FAKE * 2), "overlaps"),
+    (dict(M=1 << 20, K=1 << 12), "2^31"),
+])
+def test_invalid_arguments_rejected_before_device(kw, msg):
+    assert _fused(**kw) == mmar.EINVAL
+    assert msg in mmar.last_error()
+
+
+def test_misaligned_pointer():
+    assert _fused(W=FAKE + 8) == mmar.EALIGN
+    assert "W" in mmar.last_error()
+
+
+def test_other_entry_points_validate():
+    L = mmar.lib
+    assert L.mmar_gemm_only(FAKE, FAKE * 2, FAKE * 8, 64, 256, 250, 4, 0, 0, None) == mmar.EINVAL
+    assert L.mmar_gemm_partials(None, FAKE, FAKE, 64, 64, 64, 2, None) == mmar.EINVAL
+    assert L.mmar_reduce_epilogue_only(FAKE, FAKE, FAKE, FAKE, 64, 64, 2, 2.0, 0, None) == mmar.EINVAL
+    assert L.mmar_reduce_epilogue_only(FAKE, FAKE, FAKE, FAKE, 60, 64, 2, 0.1, 0, None) == mmar.EINVAL
+    assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 7,
+                           0, 0, 0, None, 0, None) == mmar.EINVAL
+    assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 2,
+                           0, 0, 9, None, 0, None) == mmar.EINVAL
+    assert L.mmar_set_plan(64, 256, 256, 4, 9, 0, 0, 0) == mmar.EINVAL
+    assert L.mmar_autotune(64, 256, 250, 4, 0) == mmar.EINVAL
+
+
+def test_workspace_bytes():
+    assert mmar.workspace_bytes("persistent", 8192, 3072, 12288, 16) == 0
+    assert mmar.workspace_bytes("sequential", 8192, 3072, 12288, 16) == 4 * 16 * 8192 * 3072
+    assert mmar.workspace_bytes("sequential", 64, 256, 256, 4, chunk=(32, 64)) == 4 * 4 * 32 * 64
+    assert mmar.workspace_bytes("streams", 1024, 512, 256, 4, chunk=(256, 512), ring=3) == \
+        3 * 4 * 4 * 256 * 512
+    with pytest.raises(mmar.MmarError):
+        mmar.workspace_bytes("streams", 1024, 512, 250, 4)
+
+
+def test_no_device_reports_enodev():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the no-device path is for CPU-only hosts")
+    assert _fused() == mmar.ENODEV
+    assert mmar.lib.mmar_autotune(64, 256, 256, 4, 0) == mmar.ENODEV
+    assert mmar.lib.mmar_release() == mmar.OK

@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bars: the dropout mask bit-exact; fp32 output within 2e-3 * max(1, |oracle|); output
+bits identical across chunk sizes and schedules; structure pins exact.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from workload import WORKLOADS, f32_to_bf16_bits, make_inputs, make_random_inputs
+from helpers import assert_within_tol, dev, f32_bits, host
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only machines, never run there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import chunked_matmul_reduce_amd as mmar  # noqa: E402
+
+ONE = 0x3F80
+SCHEDS = ["persistent", "sequential", "streams"]
+
+
+def _to_dev(inp):
+    return {k: dev(inp[k], torch) for k in ("X", "W", "bias", "residual")}
+
+
+def _run(d, P, p, seed, sched="auto", chunk=(0, 0), ring=0):
+    if sched == "auto":
+        out = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, p, seed, chunk=chunk)
+    else:
+        out = mmar.fused_ex(d["X"], d["W"], d["bias"], d["residual"], P, p, seed, sched,
+                            chunk=chunk, ring=ring)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def _mask_readout(M, N, K, P, p, seed, sched="auto", chunk=(0, 0)):
+    """X = 0, bias = 1, residual = 0: out is exactly 0 (dropped) or scale (kept)."""
+    X = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
+    b = torch.ones((N,), dtype=torch.bfloat16, device="cuda")
+    r = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
+    d = {"X": X, "W": W, "bias": b, "residual": r}
+    out = _run(d, P, p, seed, sched, chunk)
+    scale = np.float32(1.0 / (1.0 - float(np.float32(p))))
+    assert np.all((out == 0) | (out == scale))
+    return out != 0
+
+
+def _check_block(inp, out, rows=None):
+    ora, keep = oracle.run_inputs(inp, rows=rows)
+    res = inp["residual"] if rows is None else inp["residual"][rows]
+    o = out if rows is None else out[rows]
+    worst = assert_within_tol(o, ora)
+    # every dropped element is the residual, bit for bit
+    res32 = (res.astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(f32_bits(o[~keep]), f32_bits(res32[~keep]))
+    return worst
+
+
+# ---------------------------------------------------------------- tiny block
+def test_tiny_all_schedules_chunks_bit_identical():
+    w = WORKLOADS["tiny"]
+    inp = make_inputs("tiny")
+    d = _to_dev(inp)
+    outs = {}
+    for sched in SCHEDS:
+        for chunk in [(32, 64), (64, 64), (32, 256), (64, 256), (0, 0)]:
+            out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk)
+            outs[(sched, chunk)] = out
+            print(sched, chunk, "max rel err", _check_block(inp, out), flush=True)
+    ref = f32_bits(outs[("persistent", (32, 64))])
+    for k, o in outs.items():
+        assert np.array_equal(f32_bits(o), ref), k
+    keep = _mask_readout(w.M, w.N, w.K, w.P, inp["p_drop"], w.seed, chunk=w.chunk)
+    assert np.array_equal(keep, oracle.keep_mask(w.M, w.N, inp["p_drop"], w.seed))
+
+
+# ---------------------------------------------------------------- ragged shapes
+RAGGED = [
+    # M, K, N, P: tiles of 256 x 128 leave ragged last tiles; K/P = 96 takes the 32-wide K step
+    (800, 1536, 416, 3),
+    (288, 480, 160, 5),
+    (64, 64, 32, 1),
+    (1056, 2048, 544, 8),
+    (32, 4096, 4096, 2),
+]
+
+
+@pytest.mark.parametrize("M,K,N,P", RAGGED)
+def test_ragged_shapes_against_oracle(M, K, N, P):
+    inp = make_random_inputs(M, K, N, seed=M + K + N + P)
+    inp.update(M=M, K=K, N=N, P=P, p_drop=np.float32(0.2), seed=(M << 40) + N)
+    d = _to_dev(inp)
+    ref = None
+    for sched in SCHEDS:
+        for chunk in [(0, 0), (32, 32), (M // 2 if (M // 2) % 32 == 0 else M, N)]:
+            out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk)
+            _check_block(inp, out)
+            if ref is None:
+                ref = f32_bits(out)
+            assert np.array_equal(f32_bits(out), ref), (sched, chunk)
+
+
+# ---------------------------------------------------------------- full-size workloads
+def _sample_rows(M, rng):
+    edge = [0, 1, 31, 32, 63, 64, 255, 256, M // 2, M - 257, M - 256, M - 1]
+    return np.unique(np.concatenate([np.array(edge), rng.choice(M, size=180, replace=False)]))
+
+
+@pytest.mark.parametrize("name", ["gpt2_attn", "gpt2_mlp", "bert_mlp", "gpt3_mlp"])
+def test_full_size_workload(name):
+    """The launch configuration the benchmark times (library plan, default chunk)."""
+    w = WORKLOADS[name]
+    inp = make_inputs(name)
+    d = _to_dev(inp)
+    out = _run(d, w.P, inp["p_drop"], w.seed)
+    rows = _sample_rows(w.M, np.random.default_rng(w.seed))
+    worst = _check_block(inp, out, rows=rows)
+    keep = oracle.keep_mask(w.M, w.N, inp["p_drop"], w.seed)
+    res32 = (inp["residual"].astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(f32_bits(out[~keep]), f32_bits(res32[~keep]))
+    del d
+    torch.cuda.empty_cache()
+    gkeep = _mask_readout(w.M, w.N, w.K, w.P, inp["p_drop"], w.seed)
+    assert np.array_equal(gkeep, keep)
+    print(name, "max rel err on sampled rows", worst, "kept", keep.mean(), flush=True)
+
+
+def test_full_size_schedule_invariance():
+    w = WORKLOADS["gpt2_attn"]
+    inp = make_inputs("gpt2_attn")
+    d = _to_dev(inp)
+    ref = f32_bits(_run(d, w.P, inp["p_drop"], w.seed, "persistent"))
+    for sched, chunk, ring in [("persistent", (w.M // 2, w.N // 2), 0), ("persistent", (1024, 3072), 0),
+                               ("streams", (1024, w.N), 2), ("streams", (2048, 1536), 3),
+                               ("sequential", (0, 0), 0)]:
+        out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, ring)
+        assert np.array_equal(f32_bits(out), ref), (sched, chunk, ring)
+
+
+# ---------------------------------------------------------------- structure pins
+def _struct_inputs(P, Ks, kinds, M=32, N=32):
+    """Every output element built from the same per-slice pattern (see tests/golden)."""
+    K = P * Ks
+    xr = np.zeros(K, np.uint16)
+    wc = np.zeros(K, np.uint16)
+    for p, kind in enumerate(kinds):
+        lo = p * Ks
+        if kind in ("big", "-big"):
+            xr[lo:lo + Ks] = ONE
+            wc[lo:lo + Ks] = f32_to_bf16_bits(np.full(Ks, (2.0 ** 18) * (1 if kind == "big" else -1),
+                                                      np.float32))
+        elif kind == "unit_per_32":
+            xr[lo:lo + Ks:32] = ONE
+            wc[lo:lo + Ks:32] = ONE
+        elif kind == "one":
+            xr[lo] = ONE
+            wc[lo] = ONE
+    X = np.tile(xr, (M, 1))
+    W = np.tile(wc[:, None], (1, N))
+    z = {"bias": np.zeros(N, np.uint16), "residual": np.zeros((M, N), np.uint16)}
+    return {"X": X, "W": W, **z}
+
+
+def _golden():
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "structure_pins.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_per_slice_accumulation_exact(sched):
+    g = _golden()["per_slice_2p24"]
+    inp = _struct_inputs(2, 64, ["big", "unit_per_32"])
+    out = _run(_to_dev(inp), 2, 0.0, 0, sched)
+    assert np.all(out == np.float32(g["per_slice_fp32"]))
+
+
+@pytest.mark.parametrize("sched", SCHEDS)
+def test_slice_order_exact(sched):
+    g = _golden()["slice_order"]
+    inp = _struct_inputs(3, 64, ["big", "one", "-big"])
+    out = _run(_to_dev(inp), 3, 0.0, 0, sched)
+    assert np.all(out == np.float32(g["left_to_right_fp32"]))
+
+
+def test_p_one_is_residual_bits():
+    inp = make_random_inputs(256, 512, 384, seed=11)
+    d = _to_dev(inp)
+    res32 = (inp["residual"].astype(np.uint32) << 16).view(np.float32)
+    for sched in SCHEDS:
+        out = _run(d, 4, 1.0, 5, sched)
+        assert np.array_equal(f32_bits(out), f32_bits(res32))
+
+
+@pytest.mark.parametrize("p", [0.0, 0.1, 0.3])
+def test_epilogue_closed_form_bits(p):
+    """X = 0 so T = 0: out is the fp32 model of the epilogue, bit for bit."""
+    M, K, N, P = 96, 128, 160, 2
+    inp = make_random_inputs(M, K, N, seed=12, sigma_bias=1.0)
+    inp["X"][:] = 0
+    keep = oracle.keep_mask(M, N, p, 77)
+    want = oracle.reduce_epilogue_fp32([np.zeros((M, N))], inp["bias"], inp["residual"], keep, p)
+    d = _to_dev(inp)
+    for sched in SCHEDS:
+        out = _run(d, P, p, 77, sched)
+        assert np.array_equal(f32_bits(out), f32_bits(want)), sched
+
+
+# ---------------------------------------------------------------- measurement entry points
+def test_gemm_only_and_partials_compose_to_fused():
+    M, K, N, P = 512, 1024, 384, 4
+    inp = make_random_inputs(M, K, N, seed=13)
+    d = _to_dev(inp)
+    fused = _run(d, P, 0.1, 3, "persistent")
+    T = mmar.gemm_only(d["X"], d["W"], P)
+    o1 = mmar.reduce_epilogue_only(T[None], d["bias"], d["residual"], 0.1, 3)
+    parts = mmar.gemm_partials(d["X"], d["W"], P)
+    o2 = mmar.reduce_epilogue_only(parts, d["bias"], d["residual"], 0.1, 3)
+    torch.cuda.synchronize()
+    assert np.array_equal(f32_bits(host(o1)), f32_bits(fused))
+    assert np.array_equal(f32_bits(host(o2)), f32_bits(fused))
+    # each partial against the oracle's slice product
+    for p, Sp in enumerate(oracle.slice_partials(inp["X"], inp["W"], P)):
+        assert_within_tol(host(parts[p]), Sp, f"slice {p}")
+    # T against the oracle's reduced sum
+    assert_within_tol(host(T), sum(oracle.slice_partials(inp["X"], inp["W"], P)), "T")
+
+
+def test_repeat_caller_workspace_and_stream():
+    M, K, N, P = 512, 768, 256, 4
+    inp = make_random_inputs(M, K, N, seed=14)
+    d = _to_dev(inp)
+    ref = f32_bits(_run(d, P, 0.1, 9, "persistent"))
+    assert np.array_equal(f32_bits(_run(d, P, 0.1, 9, "persistent")), ref)
+    for sched, ring in [("sequential", 0), ("streams", 2), ("streams", 3)]:
+        nbytes = mmar.workspace_bytes(sched, M, N, K, P, chunk=(128, N), ring=ring)
+        ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        out = mmar.fused_ex(d["X"], d["W"], d["bias"], d["residual"], P, 0.1, 9, sched,
+                            chunk=(128, N), ring=ring, workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(f32_bits(host(out)), ref), sched
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, 0.1, 9)
+    s.synchronize()
+    assert np.array_equal(f32_bits(host(out)), ref)
+
+
+def test_invalid_arguments_leave_out_untouched():
+    M, K, N, P = 64, 128, 64, 2
+    inp = make_random_inputs(M, K, N, seed=15)
+    d = _to_dev(inp)
+    out = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    ptrs = [d[k].data_ptr() for k in ("X", "W", "bias", "residual")]
+    bad = [
+        dict(P=3), dict(p=1.5), dict(p=float("nan")), dict(chunk=(48, 0)), dict(chunk=(0, 40)),
+        dict(M=48), dict(P=0),
+    ]
+    for b in bad:
+        rc = mmar.lib.mmar_fused(*ptrs, out.data_ptr(), b.get("M", M), N, K, b.get("P", P),
+                                 b.get("p", 0.1), 1, *b.get("chunk", (0, 0)), None)
+        assert rc == mmar.EINVAL, (b, rc, mmar.last_error())
+    rc = mmar.lib.mmar_fused(ptrs[0] + 2, *ptrs[1:], out.data_ptr(), M, N, K, P, 0.1, 1, 0, 0, None)
+    assert rc == mmar.EALIGN
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    rc = mmar.lib.mmar_fused_ex(*ptrs, out.data_ptr(), M, N, K, P, 0.1, 1, mmar.SCHED_SEQUENTIAL,
+                                0, 0, 0, small.data_ptr(), 16, None)
+    assert rc == mmar.ENOMEM
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+def test_autotune_keeps_bits():
+    M, K, N, P = 1024, 2048, 768, 8
+    inp = make_random_inputs(M, K, N, seed=16)
+    d = _to_dev(inp)
+    ref = f32_bits(_run(d, P, 0.1, 4, "persistent"))
+    mmar.autotune(M, N, K, P, flags=1)
+    plan = mmar.get_plan(M, N, K, P)
+    print("tuned plan", plan, flush=True)
+    assert np.array_equal(f32_bits(_run(d, P, 0.1, 4)), ref)
+    mmar.set_plan(M, N, K, P, "streams", chunk=(256, N), ring=2)
+    assert mmar.get_plan(M, N, K, P)["schedule"] == mmar.SCHED_STREAMS
+    assert np.array_equal(f32_bits(_run(d, P, 0.1, 4)), ref)
+    mmar.set_plan(M, N, K, P, "auto")
+    assert mmar.get_plan(M, N, K, P)["schedule"] == mmar.SCHED_PERSISTENT
