@@ -54,6 +54,13 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python -m chunked_matmul_reduce_amd.build` (hipcc, gfx950)")
+    # PyTorch ships its own HIP runtime (same soname as ROCm's).  Load it first so that
+    # libmmar binds to the runtime torch uses: two HIP runtimes in one process do not
+    # share the device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

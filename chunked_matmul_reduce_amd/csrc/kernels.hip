@@ -93,86 +93,69 @@ __device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int
 }
 
 // ------------------------------------------------------------------ tile kernel
+#define MMAR_LDS __attribute__((address_space(3)))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 template <int BK>
 struct TileCfg {
     static constexpr int BM = kBM, BN = kBN;
-    static constexpr int NB = BN / 32;              // 32-column blocks per wave
-    static constexpr int KS = BK / 16;              // MFMA k steps per K step
-    static constexpr int LDK = BK + 8;              // padded LDS row (elements)
-    static constexpr int KB = BK / 8;               // 8-row groups of a W tile
-    static constexpr int NPT = BN * BK / (8 * kThreads);  // columns of a thread's W piece
-    static_assert(NPT == 2 || NPT == 4, "W piece is 8 k x 2 or 4 n");
+    static constexpr int NB = BN / 32;            // 32-column blocks per wave
+    static constexpr int KS = BK / 16;            // MFMA k steps per K step
+    static constexpr int STAGES = 3;              // LDS ring depth (prefetch distance 2)
+    static constexpr int XS = BM * BK;            // elements of an X stage [BM][BK]
+    static constexpr int WS = BK * BN;            // elements of a W stage [BK][BN]
+    static constexpr int CPR = BK / 8;            // 16-byte chunks per X row
+    static constexpr int XQ = 64 * BK / 8 / 64;   // DMA instructions per wave for its X rows
+    static constexpr int WQ = BK * BN / 8 / 64 / 4;   // DMA instructions per wave for W
+    static constexpr int DMA = XQ + WQ;           // DMA instructions per wave per K step
+    static constexpr int LDS_BYTES = STAGES * (XS + WS) * 2;
+    static_assert(LDS_BYTES <= 163840, "LDS budget");
 };
 
+// 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).
 template <int BK>
-__device__ __forceinline__ void load_x(uint4 (&x)[2][BK / 16], const uint16_t* const (&xrow)[2],
-                                       int64_t k) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int s = 0; s < BK / 16; ++s)
-            x[mb][s] = *reinterpret_cast<const uint4*>(xrow[mb] + k + 16 * s);
+__device__ __forceinline__ int swz_x(int m) {
+    return BK == 64 ? ((m & 7) ^ ((m >> 3) & 1)) : ((m >> 2) & 3);
+}
+__device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define MMAR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
+
+// One 16-byte global -> LDS copy per lane: lane l's bytes land at lds_addr + 16 l
+// (lds_addr is wave-uniform, passed in M0).  Written as inline asm so that the
+// compiler does not turn its LDS write into a wait on every later LDS read; the
+// kernel waits on the vector-memory counter itself.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(lds_addr)
+        : "memory");
 }
 
-// A thread's piece of the W tile: 8 consecutive k rows x NPT consecutive n columns.
-template <int NPT>
-__device__ __forceinline__ void load_w(uint32_t (&w)[8][NPT / 2], const uint16_t* wcol, int64_t k,
-                                       int64_t N) {
-    const uint16_t* p = wcol + k * N;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if constexpr (NPT == 4) {
-            const uint2 v = *reinterpret_cast<const uint2*>(p + j * N);
-            w[j][0] = v.x;
-            w[j][1] = v.y;
-        } else {
-            w[j][0] = *reinterpret_cast<const uint32_t*>(p + j * N);
-        }
-    }
-}
+// Workgroup barrier without the memory fence of __syncthreads (which would also wait
+// for the prefetches in flight); "memory" keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Transpose the piece into NPT k-contiguous 16-byte rows of the LDS tile [BN][LDK].
-template <int NPT, int LDK>
-__device__ __forceinline__ void store_w(uint16_t* lds, const uint32_t (&w)[8][NPT / 2], int nq,
-                                        int kb) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-        uint32_t d[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t a = w[2 * j][i / 2], b = w[2 * j + 1][i / 2];
-            d[j] = (i % 2 == 0) ? ((a & 0xFFFFu) | (b << 16)) : ((a >> 16) | (b & 0xFFFF0000u));
-        }
-        *reinterpret_cast<uint4*>(lds + (NPT * nq + i) * LDK + 8 * kb) =
-            make_uint4(d[0], d[1], d[2], d[3]);
-    }
-}
-
-template <int BK>
-__device__ __forceinline__ void mfma_step(f32x16 (&S)[kBN / 32][2], const uint16_t* lds,
-                                          const uint4 (&x)[2][BK / 16], int l32, int h) {
-    using C = TileCfg<BK>;
-#pragma unroll
-    for (int s = 0; s < C::KS; ++s) {
-        bf16x8 wf[C::NB];
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-            wf[nb] = *reinterpret_cast<const bf16x8*>(lds + (32 * nb + l32) * C::LDK + 16 * s + 8 * h);
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-                S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    wf[nb], __builtin_bit_cast(bf16x8, x[mb][s]), S[nb][mb], 0, 0, 0);
-    }
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const MMAR_LDS void*)p));
 }
 
 template <int MODE, int BK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void tile_kernel(TileArgs a) {
     using C = TileCfg<BK>;
-    constexpr int BM = C::BM, BN = C::BN, NB = C::NB, LDK = C::LDK, NPT = C::NPT;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][BN * LDK];
+    constexpr int BM = C::BM, BN = C::BN, NB = C::NB;
+    extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+    uint16_t* const xs_base = smem;                     // [STAGES][BM][BK]
+    uint16_t* const ws_base = smem + C::STAGES * C::XS;  // [STAGES][BK][BN]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
@@ -185,9 +168,22 @@ void tile_kernel(TileArgs a) {
     const int tpcm = (a.cm + BM - 1) / BM, tpcn = (a.cn + BN - 1) / BN, tpc = tpcm * tpcn;
     const int chunks_n = a.RN / a.cn;
     const int n_tiles = (a.RM / a.cm) * chunks_n * tpc;
-
-    const int wkb = tid % C::KB, wnq = tid / C::KB;
     const int sps = a.Ks / BK;   // K steps per slice
+
+    // Per-lane constants of the operand reads.
+    // X (B slot): row m = 64 wave + 32 mb + l32 of the tile, 16-byte chunk 2 s + h.
+    int xoff[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int m = wave * 64 + mb * 32 + l32;
+        xoff[mb] = m * BK;
+    }
+    // W (A slot) through the LDS transpose read: in each 16-lane group i = lane % 16,
+    // lane i points at row k = kb + i / 4 and columns 4 (i % 4) .. +3 of a 16-column half;
+    // the read returns to lane j column j and rows kb .. kb + 3.
+    const int gi = lane & 15, grp = lane >> 4;
+    const int wk = 8 * (grp >> 1) + (gi >> 2);          // row within the 16-row k step
+    const int wn = 16 * (grp & 1) + 4 * (gi & 3);       // column within a 32-column block
 
     for (int item = slot; item < a.total_items; item += G) {
         int tile_item = item, p_lo = 0, p_hi = a.P;
@@ -207,52 +203,93 @@ void tile_kernel(TileArgs a) {
         const int n0 = a.rn0 + cc * a.cn + tn * BN;
         const int rows = min(BM, a.cm - tm * BM), cols = min(BN, a.cn - tn * BN);
 
-        const uint16_t* xrow[2];
+        // DMA sources.  X: wave w loads its own 64 rows; instruction q, lane l covers the
+        // 16-byte LDS chunk 64 q + l of the wave's region.  W: the 4 waves split the
+        // [BK][BN] tile; instruction q of wave w covers chunks 64 (WQ w + q) + l.
+        const uint16_t* xsrc[C::XQ];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int r = min(wave * 64 + mb * 32 + l32, rows - 1);
-            xrow[mb] = a.X + static_cast<int64_t>(m0 + r) * a.K + 8 * h;
+        for (int q = 0; q < C::XQ; ++q) {
+            const int idx = 64 * q + lane;
+            const int r = idx / C::CPR, pos = idx % C::CPR;
+            const int grow = min(wave * 64 + r, rows - 1);
+            const int c = pos ^ swz_x<BK>(wave * 64 + r);
+            xsrc[q] = a.X + static_cast<int64_t>(m0 + grow) * a.K + 8 * c;
         }
-        const uint16_t* wcol =
-            a.W + static_cast<int64_t>(8 * wkb) * a.N + n0 + min(NPT * wnq, cols - NPT);
+        const uint16_t* wsrc[C::WQ];
+#pragma unroll
+        for (int q = 0; q < C::WQ; ++q) {
+            const int idx = 64 * (C::WQ * wave + q) + lane;
+            const int k = idx / (BN / 8), pos = idx % (BN / 8);
+            const int c = pos ^ swz_w(k);
+            wsrc[q] = a.W + static_cast<int64_t>(k) * a.N + n0 + min(8 * c, cols - 8);
+        }
 
+        const int nsteps = (p_hi - p_lo) * sps;
         const int64_t k_first = static_cast<int64_t>(p_lo) * a.Ks;
-        const int64_t k_last = static_cast<int64_t>(p_hi) * a.Ks - BK;   // start of the last step
+
+        const int uwave = __builtin_amdgcn_readfirstlane(wave);
+        auto issue = [&](int st) {   // DMA of K step st into stage st % STAGES
+            const int stage = st % C::STAGES;
+            const int64_t k = k_first + static_cast<int64_t>(st) * BK;
+            const uint32_t xd = lds_addr(xs_base + stage * C::XS + uwave * 64 * BK);
+#pragma unroll
+            for (int q = 0; q < C::XQ; ++q) dma16(xsrc[q] + k, xd + q * 1024);
+            const uint32_t wd = lds_addr(ws_base + stage * C::WS + C::WQ * uwave * 512);
+#pragma unroll
+            for (int q = 0; q < C::WQ; ++q) dma16(wsrc[q] + k * a.N, wd + q * 1024);
+        };
 
         f32x16 S[NB][2], T[NB][2];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb) T[nb][mb] = f32x16{};
-        uint4 xc[2][C::KS], xn[2][C::KS];
-        uint32_t wr[8][NPT / 2];
 
-        load_x<BK>(xc, xrow, k_first);
-        load_w<NPT>(wr, wcol, k_first, a.N);
-        store_w<NPT, LDK>(lds[0], wr, wnq, wkb);
-        __syncthreads();
+        issue(0);
+        if (nsteps > 1) issue(1);
 
-        int buf = 0;
-        int64_t k = k_first;
+        int st = 0;
         for (int p = p_lo; p < p_hi; ++p) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb) S[nb][mb] = f32x16{};
-            for (int j = 0; j < sps; ++j) {
-                // prefetch the next K step (the last step re-reads itself: no branch)
-                const int64_t kn = min(k + BK, k_last);
-                load_x<BK>(xn, xrow, kn);
-                load_w<NPT>(wr, wcol, kn, a.N);
-                mfma_step<BK>(S, lds[buf], xc, l32, h);
-                store_w<NPT, LDK>(lds[buf ^ 1], wr, wnq, wkb);
-                __syncthreads();
+            for (int j = 0; j < sps; ++j, ++st) {
+                // this wave's DMA for step st is complete once at most the next step's remain
+                if (st + 1 < nsteps) MMAR_WAIT_VM(C::DMA);
+                else MMAR_WAIT_VM(0);
+                wg_barrier();   // every wave's DMA for st landed; step st-1 fully consumed
+                if (st + 2 < nsteps) issue(st + 2);
+                const int stage = st % C::STAGES;
+                const uint16_t* xs = xs_base + stage * C::XS;
+                const uint16_t* wsb = ws_base + stage * C::WS;
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
+                for (int s = 0; s < C::KS; ++s) {
+                    bf16x8 xf[2], wf[NB];
 #pragma unroll
-                    for (int s = 0; s < C::KS; ++s) xc[mb][s] = xn[mb][s];
-                buf ^= 1;
-                k += BK;
+                    for (int mb = 0; mb < 2; ++mb) {
+                        const int m = wave * 64 + mb * 32 + l32;
+                        xf[mb] = *reinterpret_cast<const bf16x8*>(
+                            xs + xoff[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const int k1 = 16 * s + wk, k2 = k1 + 4;
+                        const int n = 32 * nb + wn;
+                        const uint16_t* p1 = wsb + k1 * BN + 8 * ((n >> 3) ^ swz_w(k1)) + (n & 7);
+                        const uint16_t* p2 = wsb + k2 * BN + 8 * ((n >> 3) ^ swz_w(k2)) + (n & 7);
+                        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p1);
+                        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p2);
+                        const v4i16 both[2] = {lo, hi};
+                        wf[nb] = __builtin_bit_cast(bf16x8, both);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int mb = 0; mb < 2; ++mb)
+                            S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb],
+                                                                                S[nb][mb], 0, 0, 0);
+                }
             }
             // fixed-order fp32 slice reduction: T = 0 + S_0 (= S_0 exactly, an MFMA sum
             // started from +0 is never -0), then T + S_1, T + S_2, ...
@@ -263,6 +300,7 @@ void tile_kernel(TileArgs a) {
                     for (int mb = 0; mb < 2; ++mb) T[nb][mb] += S[nb][mb];
             }
         }
+        wg_barrier();   // all waves done with the LDS ring before the next item's DMA
 
         // Store / epilogue.  Lane holds rows m = 32 mb + l32 and, in registers 4g..4g+3
         // of block nb, columns 32 nb + 8 g + 4 h + 0..3.
@@ -341,7 +379,16 @@ __global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* p, int64_t n, 
 // ------------------------------------------------------------------ launchers
 template <int MODE, int BK>
 static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((tile_kernel<MODE, BK>), dim3(grid), dim3(kThreads), 0, s, a);
+    constexpr int lds = TileCfg<BK>::LDS_BYTES;
+    static bool attr_set = false;
+    if (!attr_set) {
+        void (*fn)(TileArgs) = tile_kernel<MODE, BK>;
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL((tile_kernel<MODE, BK>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
@@ -373,8 +420,10 @@ hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hi
 template <int MODE, int BK>
 static int occ_t() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_kernel<MODE, BK>, kThreads, 0) !=
-        hipSuccess)
+    const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK>);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, fn, kThreads,
+            static_cast<size_t>(TileCfg<BK>::LDS_BYTES)) != hipSuccess)
         return 0;
     return n;
 }
