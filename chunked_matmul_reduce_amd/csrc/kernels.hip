@@ -96,20 +96,28 @@ __device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int
 #define MMAR_LDS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+#ifndef MMAR_WAVES_M
+#define MMAR_WAVES_M 4
+#endif
+
 template <int BK>
 struct TileCfg {
     static constexpr int BM = kBM, BN = kBN;
-    static constexpr int NB = BN / 32;            // 32-column blocks per wave
-    static constexpr int KS = BK / 16;            // MFMA k steps per K step
-    static constexpr int STAGES = 3;              // LDS ring depth (prefetch distance 2)
-    static constexpr int XS = BM * BK;            // elements of an X stage [BM][BK]
-    static constexpr int WS = BK * BN;            // elements of a W stage [BK][BN]
-    static constexpr int CPR = BK / 8;            // 16-byte chunks per X row
-    static constexpr int XQ = 64 * BK / 8 / 64;   // DMA instructions per wave for its X rows
-    static constexpr int WQ = BK * BN / 8 / 64 / 4;   // DMA instructions per wave for W
-    static constexpr int DMA = XQ + WQ;           // DMA instructions per wave per K step
+    static constexpr int WM = MMAR_WAVES_M;             // waves along m
+    static constexpr int WN = 4 / WM;                   // waves along n
+    static constexpr int RW = BM / WM, CW = BN / WN;    // rows / columns of a wave
+    static constexpr int MB = RW / 32, NB = CW / 32;    // 32 x 32 MFMA blocks of a wave
+    static constexpr int KS = BK / 16;                  // MFMA k steps per K step
+    static constexpr int STAGES = 3;                    // LDS ring depth (prefetch distance 2)
+    static constexpr int XS = BM * BK;                  // elements of an X stage [BM][BK]
+    static constexpr int WS = BK * BN;                  // elements of a W stage [BK][BN]
+    static constexpr int CPR = BK / 8;                  // 16-byte chunks per X row
+    static constexpr int XQ = XS / 8 / 64 / 4;          // X copy instructions per wave
+    static constexpr int WQ = WS / 8 / 64 / 4;          // W copy instructions per wave
+    static constexpr int DMA = XQ + WQ;                 // copy instructions per wave per step
     static constexpr int LDS_BYTES = STAGES * (XS + WS) * 2;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
+    static_assert(MB * NB == 8, "8 MFMA blocks per wave");
 };
 
 // 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).
@@ -119,49 +127,59 @@ __device__ __forceinline__ int swz_x(int m) {
 }
 __device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+// s_waitcnt on the vector-memory counter only (gfx9 encoding).
 #define MMAR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
 
-// One 16-byte global -> LDS copy per lane: lane l's bytes land at lds_addr + 16 l
-// (lds_addr is wave-uniform, passed in M0).  Written as inline asm so that the
-// compiler does not turn its LDS write into a wait on every later LDS read; the
-// kernel waits on the vector-memory counter itself.
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_addr) {
+// One 16-byte global -> LDS copy per lane from sbase + voff (sbase wave-uniform, voff a
+// per-lane byte offset); lane l's bytes land at lds_addr + 16 l (lds_addr wave-uniform,
+// passed in M0, which is saved and restored).  Inline asm, so that the compiler does not
+// turn its LDS write into a wait on every later LDS read; the kernel waits on the
+// vector-memory counter itself.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %2\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, off\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(src), "s"(lds_addr)
+        : "v"(voff), "s"(sbase), "s"(lds_addr)
         : "memory");
 }
 
-// Workgroup barrier without the memory fence of __syncthreads (which would also wait
-// for the prefetches in flight); "memory" keeps the compiler from moving LDS accesses
-// across it.
-__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    return reinterpret_cast<const void*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const MMAR_LDS void*)p));
 }
 
+// Workgroup barrier without the memory fence of __syncthreads (which would also wait
+// for the copies in flight); "memory" keeps the compiler from moving LDS accesses
+// across it.
+__device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
 template <int MODE, int BK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void tile_kernel(TileArgs a) {
     using C = TileCfg<BK>;
-    constexpr int BM = C::BM, BN = C::BN, NB = C::NB;
+    constexpr int BM = C::BM, BN = C::BN, NB = C::NB, MB = C::MB, KS = C::KS;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    uint16_t* const xs_base = smem;                     // [STAGES][BM][BK]
-    uint16_t* const ws_base = smem + C::STAGES * C::XS;  // [STAGES][BK][BN]
+    uint16_t* const xs_base = smem;                      // [STAGES][BM][BK], swizzled
+    uint16_t* const ws_base = smem + C::STAGES * C::XS;  // [STAGES][BK][BN], swizzled
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
+    const int wm = wave % C::WM, wn = wave / C::WM;      // this wave's block of the tile
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);
 
-    // XCD-aware slot: ids are dealt round-robin over 8 XCDs; give each XCD a contiguous
-    // run of items per sweep.
+    // XCD-aware slot: ids are dealt round-robin over the 8 XCDs; give each XCD a
+    // contiguous run of items per sweep.
     const int G = gridDim.x, bid = blockIdx.x;
     const int slot = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
 
@@ -170,20 +188,16 @@ void tile_kernel(TileArgs a) {
     const int n_tiles = (a.RM / a.cm) * chunks_n * tpc;
     const int sps = a.Ks / BK;   // K steps per slice
 
-    // Per-lane constants of the operand reads.
-    // X (B slot): row m = 64 wave + 32 mb + l32 of the tile, 16-byte chunk 2 s + h.
-    int xoff[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-        const int m = wave * 64 + mb * 32 + l32;
-        xoff[mb] = m * BK;
-    }
+    // Operand reads.  X (B slot): rows C::RW wm + 32 mb + l32, 16-byte chunk 2 s + h.
     // W (A slot) through the LDS transpose read: in each 16-lane group i = lane % 16,
-    // lane i points at row k = kb + i / 4 and columns 4 (i % 4) .. +3 of a 16-column half;
-    // the read returns to lane j column j and rows kb .. kb + 3.
+    // lane i points at row k = kb + i / 4 and columns 4 (i % 4) .. +3 of a 16-column
+    // half; the read returns to lane j column j and rows kb .. kb + 3.
+    int xrd[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) xrd[mb] = (C::RW * wm + 32 * mb + l32) * BK;
     const int gi = lane & 15, grp = lane >> 4;
-    const int wk = 8 * (grp >> 1) + (gi >> 2);          // row within the 16-row k step
-    const int wn = 16 * (grp & 1) + 4 * (gi & 3);       // column within a 32-column block
+    const int wk = 8 * (grp >> 1) + (gi >> 2);            // row within a 16-row k step
+    const int wcn = C::CW * wn + 16 * (grp & 1) + 4 * (gi & 3);   // column (block 0)
 
     for (int item = slot; item < a.total_items; item += G) {
         int tile_item = item, p_lo = 0, p_hi = a.P;
@@ -203,119 +217,150 @@ void tile_kernel(TileArgs a) {
         const int n0 = a.rn0 + cc * a.cn + tn * BN;
         const int rows = min(BM, a.cm - tm * BM), cols = min(BN, a.cn - tn * BN);
 
-        // DMA sources.  X: wave w loads its own 64 rows; instruction q, lane l covers the
-        // 16-byte LDS chunk 64 q + l of the wave's region.  W: the 4 waves split the
-        // [BK][BN] tile; instruction q of wave w covers chunks 64 (WQ w + q) + l.
-        const uint16_t* xsrc[C::XQ];
+        // Copy sources: a wave-uniform base (SGPRs) per K step plus per-lane byte
+        // offsets.  Copy q of wave w fills 16-byte chunks 64 (Q w + q) + lane of the
+        // stage; X rows are clamped to the tile, W columns to the tile.
+        uint32_t xoff[C::XQ], woff[C::WQ];
 #pragma unroll
         for (int q = 0; q < C::XQ; ++q) {
-            const int idx = 64 * q + lane;
+            const int idx = 64 * (C::XQ * wave + q) + lane;
             const int r = idx / C::CPR, pos = idx % C::CPR;
-            const int grow = min(wave * 64 + r, rows - 1);
-            const int c = pos ^ swz_x<BK>(wave * 64 + r);
-            xsrc[q] = a.X + static_cast<int64_t>(m0 + grow) * a.K + 8 * c;
+            const int c = pos ^ swz_x<BK>(r);
+            xoff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * a.K + 8 * c) * 2);
         }
-        const uint16_t* wsrc[C::WQ];
 #pragma unroll
         for (int q = 0; q < C::WQ; ++q) {
             const int idx = 64 * (C::WQ * wave + q) + lane;
             const int k = idx / (BN / 8), pos = idx % (BN / 8);
             const int c = pos ^ swz_w(k);
-            wsrc[q] = a.W + static_cast<int64_t>(k) * a.N + n0 + min(8 * c, cols - 8);
+            woff[q] = static_cast<uint32_t>((static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2);
         }
-
         const int nsteps = (p_hi - p_lo) * sps;
         const int64_t k_first = static_cast<int64_t>(p_lo) * a.Ks;
+        const uint16_t* xbase = static_cast<const uint16_t*>(
+            uniform_ptr(a.X + static_cast<int64_t>(m0) * a.K + k_first));
+        const uint16_t* wbase = static_cast<const uint16_t*>(
+            uniform_ptr(a.W + k_first * a.N + n0));
 
-        const int uwave = __builtin_amdgcn_readfirstlane(wave);
-        auto issue = [&](int st) {   // DMA of K step st into stage st % STAGES
+        // copy i (0 .. DMA-1) of K step st into stage st % STAGES: X copies first, then W
+        auto copy = [&](int st, int i) {
             const int stage = st % C::STAGES;
-            const int64_t k = k_first + static_cast<int64_t>(st) * BK;
-            const uint32_t xd = lds_addr(xs_base + stage * C::XS + uwave * 64 * BK);
-#pragma unroll
-            for (int q = 0; q < C::XQ; ++q) dma16(xsrc[q] + k, xd + q * 1024);
-            const uint32_t wd = lds_addr(ws_base + stage * C::WS + C::WQ * uwave * 512);
-#pragma unroll
-            for (int q = 0; q < C::WQ; ++q) dma16(wsrc[q] + k * a.N, wd + q * 1024);
+            if (i < C::XQ) {
+                const uint32_t xd = lds_addr(xs_base + stage * C::XS + (C::XQ * uwave + i) * 512);
+                dma16(xbase + static_cast<int64_t>(st) * BK, xoff[i], xd);
+            } else {
+                const int q = i - C::XQ;
+                const uint32_t wd = lds_addr(ws_base + stage * C::WS + (C::WQ * uwave + q) * 512);
+                dma16(wbase + static_cast<int64_t>(st) * BK * a.N, woff[q], wd);
+            }
         };
 
-        f32x16 S[NB][2], T[NB][2];
+        f32x16 S[NB][MB], T[NB][MB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) T[nb][mb] = f32x16{};
+            for (int mb = 0; mb < MB; ++mb) {
+                S[nb][mb] = f32x16{};
+                T[nb][mb] = f32x16{};
+            }
 
-        issue(0);
-        if (nsteps > 1) issue(1);
+        const int last = nsteps - 1;
+#pragma unroll
+        for (int i = 0; i < C::DMA; ++i) copy(0, i);
+#pragma unroll
+        for (int i = 0; i < C::DMA; ++i) copy(min(1, last), i);
 
         int st = 0;
         for (int p = p_lo; p < p_hi; ++p) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+          for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) S[nb][mb] = f32x16{};
-            for (int j = 0; j < sps; ++j, ++st) {
-                // this wave's DMA for step st is complete once at most the next step's remain
-                if (st + 1 < nsteps) MMAR_WAIT_VM(C::DMA);
-                else MMAR_WAIT_VM(0);
-                wg_barrier();   // every wave's DMA for st landed; step st-1 fully consumed
-                if (st + 2 < nsteps) issue(st + 2);
-                const int stage = st % C::STAGES;
-                const uint16_t* xs = xs_base + stage * C::XS;
-                const uint16_t* wsb = ws_base + stage * C::WS;
+            for (int mb = 0; mb < MB; ++mb) S[nb][mb] = f32x16{};
+          for (int j = 0; j < sps; ++j, ++st) {
+            // this wave's copies of step st are done once at most one step's remain
+            MMAR_WAIT_VM(C::DMA);
+            wg_barrier();   // every wave's copies of st landed; step st-1 fully consumed
+            // copies of step st+2 (the last steps re-copy the last one: identical bytes,
+            // no branch) are spread over the MFMAs below
+            const int st2 = min(st + 2, last);
+
+            const int stage = st % C::STAGES;
+            const uint16_t* xs = xs_base + stage * C::XS;
+            const uint16_t* wsb = ws_base + stage * C::WS;
+            auto frags = [&](int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
 #pragma unroll
-                for (int s = 0; s < C::KS; ++s) {
-                    bf16x8 xf[2], wf[NB];
-#pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) {
-                        const int m = wave * 64 + mb * 32 + l32;
-                        xf[mb] = *reinterpret_cast<const bf16x8*>(
-                            xs + xoff[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const int k1 = 16 * s + wk, k2 = k1 + 4;
-                        const int n = 32 * nb + wn;
-                        const uint16_t* p1 = wsb + k1 * BN + 8 * ((n >> 3) ^ swz_w(k1)) + (n & 7);
-                        const uint16_t* p2 = wsb + k2 * BN + 8 * ((n >> 3) ^ swz_w(k2)) + (n & 7);
-                        const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p1);
-                        const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p2);
-                        const v4i16 both[2] = {lo, hi};
-                        wf[nb] = __builtin_bit_cast(bf16x8, both);
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                        for (int mb = 0; mb < 2; ++mb)
-                            S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb],
-                                                                                S[nb][mb], 0, 0, 0);
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int m = C::RW * wm + 32 * mb + l32;
+                    xf[mb] = *reinterpret_cast<const bf16x8*>(
+                        xs + xrd[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
                 }
-            }
-            // fixed-order fp32 slice reduction: T = 0 + S_0 (= S_0 exactly, an MFMA sum
-            // started from +0 is never -0), then T + S_1, T + S_2, ...
-            if (MODE != kModePartials) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int k1 = 16 * s + wk, k2 = k1 + 4;
+                    const int n = wcn + 32 * nb;
+                    const uint16_t* p1 = wsb + k1 * BN + 8 * ((n >> 3) ^ swz_w(k1)) + (n & 7);
+                    const uint16_t* p2 = wsb + k2 * BN + 8 * ((n >> 3) ^ swz_w(k2)) + (n & 7);
+                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p1);
+                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p2);
+                    const v4i16 both[2] = {lo, hi};
+                    wf[nb] = __builtin_bit_cast(bf16x8, both);
+                }
+            };
+            // the 8 MFMAs of k step s, with the copies c0 .. c1-1 issued between them
+            auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1) {
+                int c = c0;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) T[nb][mb] += S[nb][mb];
+                    for (int mb = 0; mb < MB; ++mb) {
+                        S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb],
+                                                                            S[nb][mb], 0, 0, 0);
+                        if (((nb * MB + mb) & 1) && c < c1) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            copy(st2, c++);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+            };
+            constexpr int CPS = (C::DMA + KS - 1) / KS;   // copies per k step
+            // fragments one MFMA k step ahead of the MFMAs that use them
+            bf16x8 xa[MB], wa[NB], xb2[MB], wb2[NB];
+            frags(0, xa, wa);
+#pragma unroll
+            for (int s = 0; s < KS; s += 2) {
+                if (s + 1 < KS) frags(s + 1, xb2, wb2);
+                mfmas(xa, wa, min(s * CPS, C::DMA), min((s + 1) * CPS, C::DMA));
+                if (s + 2 < KS) frags(s + 2, xa, wa);
+                if (s + 1 < KS)
+                    mfmas(xb2, wb2, min((s + 1) * CPS, C::DMA), min((s + 2) * CPS, C::DMA));
             }
+          }
+          if (MODE != kModePartials) {
+              // T = 0 + S_0 (= S_0 exactly: an MFMA sum started from +0 is never -0),
+              // then T + S_1, T + S_2, ... in fp32, round to nearest even
+#pragma unroll
+              for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                  for (int mb = 0; mb < MB; ++mb) T[nb][mb] += S[nb][mb];
+          }
         }
-        wg_barrier();   // all waves done with the LDS ring before the next item's DMA
+        MMAR_WAIT_VM(0);
+        wg_barrier();   // every wave is done with the LDS ring before the next item's copies
 
-        // Store / epilogue.  Lane holds rows m = 32 mb + l32 and, in registers 4g..4g+3
-        // of block nb, columns 32 nb + 8 g + 4 h + 0..3.
+        // Store / epilogue.  Lane holds rows RW wm + 32 mb + l32 and, in registers
+        // 4g..4g+3 of block nb, columns CW wn + 32 nb + 8 g + 4 h + 0..3.
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int nl = 32 * nb + 8 * g + 4 * h;
+                const int nl = C::CW * wn + 32 * nb + 8 * g + 4 * h;
                 if (nl >= cols) continue;
                 const int64_t n = n0 + nl;
                 uint2 bb = make_uint2(0u, 0u);
                 if (MODE == kModeFused) bb = *reinterpret_cast<const uint2*>(a.bias + n);
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const int ml = wave * 64 + mb * 32 + l32;
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int ml = C::RW * wm + 32 * mb + l32;
                     if (ml >= rows) continue;
                     const int64_t m = m0 + ml;
                     const f32x16& acc = (MODE == kModePartials) ? S[nb][mb] : T[nb][mb];

@@ -303,7 +303,16 @@ struct Call {
     DropParams drop;
 };
 
-int bk_for(const Shape& s) { return ((s.K / s.P) % 64 == 0) ? 64 : 32; }
+// K step of the tile kernel: 64 when it divides K/P, else 32.  MMAR_FORCE_BK=32 selects
+// the 32-wide step (deeper X prefetch, twice the barriers) for measurements.
+int bk_for(const Shape& s) {
+    static const int forced = [] {
+        const char* e = std::getenv("MMAR_FORCE_BK");
+        return e ? std::atoi(e) : 0;
+    }();
+    if (forced == 32) return 32;
+    return ((s.K / s.P) % 64 == 0) ? 64 : 32;
+}
 
 int grid_for(const DevState* st, int mode, int bk, int items) {
     int occ = st->occ[mode][bk == 64 ? 0 : 1];
