@@ -158,7 +158,8 @@ def main():
         "config": {"workload": f"{w.name}: {w.desc}", "M": w.M, "K": w.K, "N": w.N, "P": P,
                    "p_drop": p, "seed": seed, "out_dtype": "fp32", "accumulate": "fp32",
                    "plan": {"schedule": {1: "sequential", 2: "streams", 3: "persistent"}[plan["schedule"]],
-                            "chunk": list(plan["chunk"]), "ring": plan["ring"]}},
+                            "chunk": list(plan["chunk"]), "ring": plan["ring"],
+                            "w_mode": {0: "direct", 1: "pretranspose"}[plan["w_mode"]]}},
     }
     with open(os.path.join(ROOT, "chunked_matmul_reduce_amd", "csrc", "kernels.hip"), "rb") as f:
         ksha = hashlib.sha256(f.read()).hexdigest()
@@ -166,7 +167,8 @@ def main():
     result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                           "traffic": _traffic(ksha),
-                          "kernel": "mmar::tile_kernel<kModeFused, 64> (persistent, one launch per step)",
+                          "kernel": "mmar::tile_kernel<kModeFused, 64, *> (persistent; with a "
+                                    "pre-transposed W the step also runs the transpose kernel)",
                           "per_launch": f"2*M*N*K = {w.flops} flop"}
     result["pct_bf16_peak"] = round(100 * value / PEAK_BF16_TFLOPS, 2)
 
@@ -184,6 +186,14 @@ def main():
         t_seq = _ev_time(torch, lambda: mmar.sequential(X, W, bias, res, P, p, seed, out=out), reps)[0]
         t_str = _ev_time(torch, lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "streams", out=out),
                          reps)[0]
+        t_dir = _ev_time(torch, lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "persistent",
+                                                      w_mode="direct", out=out), reps)[0]
+        t_pre = _ev_time(torch, lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "persistent",
+                                                      w_mode="pretranspose", out=out), reps)[0]
+        Wt = mmar.transpose_weight(W)
+        t_tr = _ev_time(torch, lambda: mmar.transpose_weight(W, out=Wt), reps)[0]
+        t_nt = _ev_time(torch, lambda: mmar.fused_nt(X, Wt, bias, res, P, p, seed, out=out), reps)[0]
+        del Wt
         del parts
         torch.cuda.empty_cache()
         re_bytes = (4 * P + 6) * w.M * w.N + 2 * w.N
@@ -191,7 +201,9 @@ def main():
         result["times_us"] = {k: round(v * 1e3, 2) for k, v in
                               {"fused": t_fused, "gemm_alone": t_gemm, "partials_gemm": t_parts,
                                "re_alone": t_re, "epi_alone": t_epi, "sequential": t_seq,
-                               "streams": t_str}.items()}
+                               "streams": t_str, "persistent_w_direct": t_dir,
+                               "persistent_w_pretranspose": t_pre, "w_transpose": t_tr,
+                               "persistent_w_given_transposed": t_nt}.items()}
         result["hidden_fraction"] = round(1.0 - (t_fused - t_gemm) / t_re, 4)
         result["hidden_fraction_epilogue"] = round(1.0 - (t_fused - t_gemm) / t_epi, 4)
         result["speedup_vs_sequential"] = round(t_seq / t_fused, 3)

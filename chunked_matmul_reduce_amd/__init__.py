@@ -3,7 +3,7 @@
 Argument marshalling only: every step of the block runs in the HIP kernels behind the C
 ABI of ``include/mmar.h``.  PyTorch supplies device memory and the current HIP stream.
 Importing this package fails if ``libmmar.so`` has not been built
-(``python -m chunked_matmul_reduce_amd.build``); there is no fallback.
+(``python chunked_matmul_reduce_amd/build.py``); there is no fallback.
 
 Block computed (see include/mmar.h for the full contract):
     out = residual + dropout_p(bias + sum_p X[:, K_p] @ W[K_p, :])     (fp32 out)
@@ -23,6 +23,8 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mmar.h")
 OK, EINVAL, EALIGN, ENODEV, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
 SCHED_AUTO, SCHED_SEQUENTIAL, SCHED_STREAMS, SCHED_PERSISTENT = 0, 1, 2, 3
 SCHEDULES = {"auto": 0, "sequential": 1, "streams": 2, "persistent": 3}
+W_AUTO, W_DIRECT, W_PRETRANSPOSE = -1, 0, 1
+W_MODES = {"auto": -1, "direct": 0, "pretranspose": 1}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -33,17 +35,19 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "mmar_fused": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
-    "mmar_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32]),
+    "mmar_fused_nt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
+    "mmar_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32]),
     "mmar_fused_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32,
-                                     _I32, _I32, _P, _SZ, _P]),
+                                     _I32, _I32, _I32, _P, _SZ, _P]),
+    "mmar_transpose_weight": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "mmar_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_gemm_only": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "mmar_gemm_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "mmar_reduce_epilogue_only": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _F, _U64, _P]),
     "mmar_autotune": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.c_uint32]),
-    "mmar_set_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32]),
+    "mmar_set_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32]),
     "mmar_get_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
-                                     ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+                                     ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
     "mmar_last_error": (ctypes.c_char_p, []),
     "mmar_version": (ctypes.c_char_p, []),
     "mmar_release": (ctypes.c_int, []),
@@ -53,7 +57,7 @@ _SIGNATURES = {
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m chunked_matmul_reduce_amd.build` (hipcc, gfx950)")
+                          "`python chunked_matmul_reduce_amd/build.py` (hipcc, gfx950)")
     # PyTorch ships its own HIP runtime (same soname as ROCm's).  Load it first so that
     # libmmar binds to the runtime torch uses: two HIP runtimes in one process do not
     # share the device.
@@ -174,11 +178,13 @@ def fused(X, W, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, stream=
 
 
 def fused_ex(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0), ring=0,
-             workspace=None, out=None, stream=None):
-    """mmar_fused_ex: every choice explicit; ``workspace`` is an optional uint8 GPU tensor."""
+             w_mode="auto", workspace=None, out=None, stream=None):
+    """mmar_fused_ex: every choice explicit; ``workspace`` is an optional GPU tensor."""
     torch = _torch()
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
+    if isinstance(w_mode, str):
+        w_mode = W_MODES[w_mode]
     M, N, K = _shapes(X, W, P)
     out = _out(out, (M, N), X)
     ws_ptr, ws_bytes = None, 0
@@ -190,7 +196,38 @@ def fused_ex(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0), ring
         rc = lib.mmar_fused_ex(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), _bits(bias, "bias", (N,)),
                                _bits(residual, "residual", (M, N)), out.data_ptr(), M, N, K, int(P),
                                float(p_drop), int(seed) & (2 ** 64 - 1), int(schedule), int(chunk[0]),
-                               int(chunk[1]), int(ring), ws_ptr, ws_bytes, _stream(X.device, stream))
+                               int(chunk[1]), int(ring), int(w_mode), ws_ptr, ws_bytes,
+                               _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def fused_nt(X, Wt, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, stream=None):
+    """mmar_fused_nt: the block with the weight given transposed, Wt = W^T [N, K]."""
+    torch = _torch()
+    if X.dim() != 2 or Wt.dim() != 2 or Wt.shape[1] != X.shape[1]:
+        raise ValueError("X must be [M, K] and Wt [N, K]")
+    M, K = (int(v) for v in X.shape)
+    N = int(Wt.shape[0])
+    out = _out(out, (M, N), X)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_fused_nt(_bits(X, "X", (M, K)), _bits(Wt, "Wt", (N, K)), _bits(bias, "bias", (N,)),
+                               _bits(residual, "residual", (M, N)), out.data_ptr(), M, N, K, int(P),
+                               float(p_drop), int(seed) & (2 ** 64 - 1), int(chunk[0]), int(chunk[1]),
+                               _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def transpose_weight(W, out=None, stream=None):
+    """mmar_transpose_weight: W [K, N] -> W^T [N, K] (bf16)."""
+    torch = _torch()
+    K, N = (int(v) for v in W.shape)
+    if out is None:
+        out = torch.empty((N, K), dtype=W.dtype, device=W.device)
+    with torch.cuda.device(W.device):
+        rc = lib.mmar_transpose_weight(_bits(W, "W", (K, N)), _bits(out, "Wt", (N, K)), K, N,
+                                       _stream(W.device, stream))
     _check(rc)
     return out
 
@@ -251,11 +288,13 @@ def reduce_epilogue_only(partials, bias, residual, p_drop, seed, out=None, strea
     return out
 
 
-def workspace_bytes(schedule, M, N, K, P, chunk=(0, 0), ring=0) -> int:
+def workspace_bytes(schedule, M, N, K, P, chunk=(0, 0), ring=0, w_mode="auto") -> int:
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
+    if isinstance(w_mode, str):
+        w_mode = W_MODES[w_mode]
     n = lib.mmar_workspace_bytes(int(schedule), int(M), int(N), int(K), int(P), int(chunk[0]),
-                                 int(chunk[1]), int(ring))
+                                 int(chunk[1]), int(ring), int(w_mode))
     if n == 0 and last_error():
         raise MmarError(EINVAL, last_error())
     return int(n)
@@ -265,15 +304,17 @@ def autotune(M, N, K, P, flags=0) -> None:
     _check(lib.mmar_autotune(int(M), int(N), int(K), int(P), int(flags)))
 
 
-def set_plan(M, N, K, P, schedule, chunk=(0, 0), ring=0) -> None:
+def set_plan(M, N, K, P, schedule, chunk=(0, 0), ring=0, w_mode="auto") -> None:
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
+    if isinstance(w_mode, str):
+        w_mode = W_MODES[w_mode]
     _check(lib.mmar_set_plan(int(M), int(N), int(K), int(P), int(schedule), int(chunk[0]),
-                             int(chunk[1]), int(ring)))
+                             int(chunk[1]), int(ring), int(w_mode)))
 
 
 def get_plan(M, N, K, P):
-    s, cm, cn, r = _I32(), _I32(), _I32(), _I32()
+    s, cm, cn, r, wm = _I32(), _I32(), _I32(), _I32(), _I32()
     _check(lib.mmar_get_plan(int(M), int(N), int(K), int(P), ctypes.byref(s), ctypes.byref(cm),
-                             ctypes.byref(cn), ctypes.byref(r)))
-    return {"schedule": s.value, "chunk": (cm.value, cn.value), "ring": r.value}
+                             ctypes.byref(cn), ctypes.byref(r), ctypes.byref(wm)))
+    return {"schedule": s.value, "chunk": (cm.value, cn.value), "ring": r.value, "w_mode": wm.value}

@@ -1,6 +1,7 @@
 """Builds libmmar.so (the gfx950 kernels and the C ABI of include/mmar.h) in place.
 
-    python -m chunked_matmul_reduce_amd.build        # from the repository root
+    python chunked_matmul_reduce_amd/build.py       # from the repository root (a script:
+                                                     # the package itself needs the library)
 
 hipcc cross-compiles for gfx950 without a GPU.  Flags: -O3; -ffp-contract=off so that
 no multiply-add in the epilogue is fused (the output bits must not depend on the

@@ -108,14 +108,15 @@ struct TileCfg {
     static constexpr int RW = BM / WM, CW = BN / WN;    // rows / columns of a wave
     static constexpr int MB = RW / 32, NB = CW / 32;    // 32 x 32 MFMA blocks of a wave
     static constexpr int KS = BK / 16;                  // MFMA k steps per K step
-    static constexpr int STAGES = 3;                    // LDS ring depth (prefetch distance 2)
+    static constexpr int XSTAGES = 3;                   // X ring depth (copies 2 steps ahead)
+    static constexpr int WSTAGES = 4;                   // W ring depth (one more: early barrier)
     static constexpr int XS = BM * BK;                  // elements of an X stage [BM][BK]
     static constexpr int WS = BK * BN;                  // elements of a W stage [BK][BN]
     static constexpr int CPR = BK / 8;                  // 16-byte chunks per X row
     static constexpr int XQ = XS / 8 / 64 / 4;          // X copy instructions per wave
     static constexpr int WQ = WS / 8 / 64 / 4;          // W copy instructions per wave
     static constexpr int DMA = XQ + WQ;                 // copy instructions per wave per step
-    static constexpr int LDS_BYTES = STAGES * (XS + WS) * 2;
+    static constexpr int LDS_BYTES = (XSTAGES * XS + WSTAGES * WS) * 2;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
     static_assert(MB * NB == 8, "8 MFMA blocks per wave");
 };
@@ -164,14 +165,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // across it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int MODE, int BK>
+// WT = false: W is [K, N] (n contiguous) and its MFMA operand is read with the LDS
+// transpose read; WT = true: W is given transposed, [N, K] (k contiguous, the layout of
+// a Linear layer's weight), and both operands use plain 16-byte LDS reads.
+template <int MODE, int BK, bool WT>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void tile_kernel(TileArgs a) {
     using C = TileCfg<BK>;
     constexpr int BM = C::BM, BN = C::BN, NB = C::NB, MB = C::MB, KS = C::KS;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-    uint16_t* const xs_base = smem;                      // [STAGES][BM][BK], swizzled
-    uint16_t* const ws_base = smem + C::STAGES * C::XS;  // [STAGES][BK][BN], swizzled
+    uint16_t* const xs_base = smem;                       // [XSTAGES][BM][BK], swizzled
+    uint16_t* const ws_base = smem + C::XSTAGES * C::XS;  // [WSTAGES][BK][BN] or [BN][BK]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, h = lane >> 5;
@@ -231,27 +235,35 @@ void tile_kernel(TileArgs a) {
 #pragma unroll
         for (int q = 0; q < C::WQ; ++q) {
             const int idx = 64 * (C::WQ * wave + q) + lane;
-            const int k = idx / (BN / 8), pos = idx % (BN / 8);
-            const int c = pos ^ swz_w(k);
-            woff[q] = static_cast<uint32_t>((static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2);
+            if constexpr (WT) {   // W^T rows n, swizzled like X
+                const int r = idx / C::CPR, pos = idx % C::CPR;
+                const int c = pos ^ swz_x<BK>(r);
+                woff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, cols - 1)) * a.K + 8 * c) * 2);
+            } else {
+                const int k = idx / (BN / 8), pos = idx % (BN / 8);
+                const int c = pos ^ swz_w(k);
+                woff[q] = static_cast<uint32_t>((static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2);
+            }
         }
         const int nsteps = (p_hi - p_lo) * sps;
         const int64_t k_first = static_cast<int64_t>(p_lo) * a.Ks;
         const uint16_t* xbase = static_cast<const uint16_t*>(
             uniform_ptr(a.X + static_cast<int64_t>(m0) * a.K + k_first));
-        const uint16_t* wbase = static_cast<const uint16_t*>(
-            uniform_ptr(a.W + k_first * a.N + n0));
+        const uint16_t* wbase = static_cast<const uint16_t*>(uniform_ptr(
+            WT ? a.W + static_cast<int64_t>(n0) * a.K + k_first : a.W + k_first * a.N + n0));
+        const int64_t wstep = WT ? BK : static_cast<int64_t>(BK) * a.N;   // per K step
 
-        // copy i (0 .. DMA-1) of K step st into stage st % STAGES: X copies first, then W
+        // copy i (0 .. DMA-1) of K step st into its stages: X copies first, then W
         auto copy = [&](int st, int i) {
-            const int stage = st % C::STAGES;
             if (i < C::XQ) {
-                const uint32_t xd = lds_addr(xs_base + stage * C::XS + (C::XQ * uwave + i) * 512);
+                const uint32_t xd = lds_addr(xs_base + (st % C::XSTAGES) * C::XS +
+                                             (C::XQ * uwave + i) * 512);
                 dma16(xbase + static_cast<int64_t>(st) * BK, xoff[i], xd);
             } else {
                 const int q = i - C::XQ;
-                const uint32_t wd = lds_addr(ws_base + stage * C::WS + (C::WQ * uwave + q) * 512);
-                dma16(wbase + static_cast<int64_t>(st) * BK * a.N, woff[q], wd);
+                const uint32_t wd = lds_addr(ws_base + (st % C::WSTAGES) * C::WS +
+                                             (C::WQ * uwave + q) * 512);
+                dma16(wbase + st * wstep, woff[q], wd);
             }
         };
 
@@ -265,37 +277,23 @@ void tile_kernel(TileArgs a) {
             }
 
         const int last = nsteps - 1;
+        // operand fragments of MFMA k step s of K step t
+        auto frags = [&](int t, int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
+            const uint16_t* xs = xs_base + (t % C::XSTAGES) * C::XS;
+            const uint16_t* wsb = ws_base + (t % C::WSTAGES) * C::WS;
 #pragma unroll
-        for (int i = 0; i < C::DMA; ++i) copy(0, i);
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = C::RW * wm + 32 * mb + l32;
+                xf[mb] = *reinterpret_cast<const bf16x8*>(
+                    xs + xrd[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
+            }
 #pragma unroll
-        for (int i = 0; i < C::DMA; ++i) copy(min(1, last), i);
-
-        int st = 0;
-        for (int p = p_lo; p < p_hi; ++p) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) S[nb][mb] = f32x16{};
-          for (int j = 0; j < sps; ++j, ++st) {
-            // this wave's copies of step st are done once at most one step's remain
-            MMAR_WAIT_VM(C::DMA);
-            wg_barrier();   // every wave's copies of st landed; step st-1 fully consumed
-            // copies of step st+2 (the last steps re-copy the last one: identical bytes,
-            // no branch) are spread over the MFMAs below
-            const int st2 = min(st + 2, last);
-
-            const int stage = st % C::STAGES;
-            const uint16_t* xs = xs_base + stage * C::XS;
-            const uint16_t* wsb = ws_base + stage * C::WS;
-            auto frags = [&](int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const int m = C::RW * wm + 32 * mb + l32;
-                    xf[mb] = *reinterpret_cast<const bf16x8*>(
-                        xs + xrd[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
-                }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
+                if constexpr (WT) {
+                    const int n = C::CW * wn + 32 * nb + l32;
+                    wf[nb] = *reinterpret_cast<const bf16x8*>(
+                        wsb + n * BK + 8 * ((2 * s + h) ^ swz_x<BK>(n)));
+                } else {
                     const int k1 = 16 * s + wk, k2 = k1 + 4;
                     const int n = wcn + 32 * nb;
                     const uint16_t* p1 = wsb + k1 * BN + 8 * ((n >> 3) ^ swz_w(k1)) + (n & 7);
@@ -305,8 +303,40 @@ void tile_kernel(TileArgs a) {
                     const v4i16 both[2] = {lo, hi};
                     wf[nb] = __builtin_bit_cast(bf16x8, both);
                 }
-            };
-            // the 8 MFMAs of k step s, with the copies c0 .. c1-1 issued between them
+            }
+        };
+        // Step-boundary handshake for K step t: this wave's copies of t are done (only the
+        // copies of the following step may remain) and the barrier makes every wave's
+        // copies of t visible; it also shows that every wave finished step t-2, whose W
+        // stage the copies issued next (for step t+2) reuse.
+        auto handshake = [&]() {
+            MMAR_WAIT_VM(C::DMA);
+            wg_barrier();
+        };
+
+#pragma unroll
+        for (int i = 0; i < C::DMA; ++i) copy(0, i);
+#pragma unroll
+        for (int i = 0; i < C::DMA; ++i) copy(min(1, last), i);
+        handshake();
+
+        // fragments are double-buffered: k step s of any K step uses buffer s % 2 (KS is
+        // even), and the first fragments of step t+1 are read during the last MFMAs of t
+        bf16x8 xa[MB], wa[NB], xb2[MB], wb2[NB];
+        frags(0, 0, xa, wa);
+
+        int st = 0;
+        for (int p = p_lo; p < p_hi; ++p) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) S[nb][mb] = f32x16{};
+          for (int j = 0; j < sps; ++j, ++st) {
+            // copies of step st+2 (the last steps re-copy the last one: identical bytes,
+            // no branch), spread over the MFMAs of k steps 0 .. KS-2
+            const int st2 = min(st + 2, last);
+            // the 8 MFMAs of one k step, with copies c0 .. c1-1 issued between them (all of
+            // them: the caller passes c1 - c0 <= DMA)
             auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1) {
                 int c = c0;
 #pragma unroll
@@ -315,24 +345,30 @@ void tile_kernel(TileArgs a) {
                     for (int mb = 0; mb < MB; ++mb) {
                         S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb],
                                                                             S[nb][mb], 0, 0, 0);
-                        if (((nb * MB + mb) & 1) && c < c1) {
+                        // spread the copies evenly over the 8 MFMAs
+                        const int upto = c0 + ((nb * MB + mb + 1) * (c1 - c0) + 7) / 8;
+                        while (c < upto) {
                             __builtin_amdgcn_sched_barrier(0);
                             copy(st2, c++);
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
             };
-            constexpr int CPS = (C::DMA + KS - 1) / KS;   // copies per k step
-            // fragments one MFMA k step ahead of the MFMAs that use them
-            bf16x8 xa[MB], wa[NB], xb2[MB], wb2[NB];
-            frags(0, xa, wa);
+            constexpr int CPS = (C::DMA + KS - 2) / (KS - 1);   // copies per k step
 #pragma unroll
             for (int s = 0; s < KS; s += 2) {
-                if (s + 1 < KS) frags(s + 1, xb2, wb2);
+                // k step s (buffer a), prefetching s+1 into buffer b
+                frags(st, s + 1, xb2, wb2);
                 mfmas(xa, wa, min(s * CPS, C::DMA), min((s + 1) * CPS, C::DMA));
-                if (s + 2 < KS) frags(s + 2, xa, wa);
-                if (s + 1 < KS)
+                // k step s+1 (buffer b), prefetching s+2, or the next K step's first
+                if (s + 2 < KS) {
+                    frags(st, s + 2, xa, wa);
                     mfmas(xb2, wb2, min((s + 1) * CPS, C::DMA), min((s + 2) * CPS, C::DMA));
+                } else {
+                    handshake();
+                    frags(min(st + 1, last), 0, xa, wa);
+                    mfmas(xb2, wb2, C::DMA, C::DMA);
+                }
             }
           }
           if (MODE != kModePartials) {
@@ -405,6 +441,39 @@ __global__ __launch_bounds__(256) void reduce_epilogue_kernel(ReduceArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ W -> W^T
+// [K, N] -> [N, K] bf16 through a padded 64 x 64 LDS tile: 16-byte coalesced loads of
+// W rows and 16-byte coalesced stores of W^T rows.  K and N are multiples of 8.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ W,
+                                                        uint16_t* __restrict__ Wt, int64_t K,
+                                                        int64_t N) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int64_t k0 = static_cast<int64_t>(blockIdx.y) * 64, n0 = static_cast<int64_t>(blockIdx.x) * 64;
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {   // 64 rows x 8 chunks of 8 elements
+        const int idx = t + 256 * r, row = idx / 8, ch = idx % 8;
+        const int64_t k = k0 + row, n = n0 + 8 * ch;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
+        if (k < K && n < N) v = *reinterpret_cast<const uint4*>(W + k * N + n);
+        const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[row][8 * ch + i] = e[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int idx = t + 256 * r, col = idx / 8, ch = idx % 8;
+        const int64_t n = n0 + col, k = k0 + 8 * ch;
+        if (n < N && k < K) {
+            uint16_t e[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) e[i] = tile[8 * ch + i][col];
+            *reinterpret_cast<uint4*>(Wt + n * K + k) = *reinterpret_cast<const uint4*>(e);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ fill (tuner inputs)
 __global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* p, int64_t n, uint32_t salt,
                                                         float amp) {
@@ -422,34 +491,46 @@ __global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* p, int64_t n, 
 }
 
 // ------------------------------------------------------------------ launchers
-template <int MODE, int BK>
+template <int MODE, int BK, bool WT>
 static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
     constexpr int lds = TileCfg<BK>::LDS_BYTES;
     static bool attr_set = false;
     if (!attr_set) {
-        void (*fn)(TileArgs) = tile_kernel<MODE, BK>;
+        void (*fn)(TileArgs) = tile_kernel<MODE, BK, WT>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set = true;
     }
-    hipLaunchKernelGGL((tile_kernel<MODE, BK>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((tile_kernel<MODE, BK, WT>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_tile(int mode, int bk, const TileArgs& a, int grid, hipStream_t s) {
+template <bool WT>
+static hipError_t launch_tile_w(int mode, int bk, const TileArgs& a, int grid, hipStream_t s) {
     if (bk == 64) {
-        if (mode == kModeFused) return launch_tile_t<kModeFused, 64>(a, grid, s);
-        if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64>(a, grid, s);
-        return launch_tile_t<kModePartials, 64>(a, grid, s);
+        if (mode == kModeFused) return launch_tile_t<kModeFused, 64, WT>(a, grid, s);
+        if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64, WT>(a, grid, s);
+        return launch_tile_t<kModePartials, 64, WT>(a, grid, s);
     }
-    if (mode == kModeFused) return launch_tile_t<kModeFused, 32>(a, grid, s);
-    if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32>(a, grid, s);
-    return launch_tile_t<kModePartials, 32>(a, grid, s);
+    if (mode == kModeFused) return launch_tile_t<kModeFused, 32, WT>(a, grid, s);
+    if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32, WT>(a, grid, s);
+    return launch_tile_t<kModePartials, 32, WT>(a, grid, s);
+}
+
+hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, hipStream_t s) {
+    return wt ? launch_tile_w<true>(mode, bk, a, grid, s) : launch_tile_w<false>(mode, bk, a, grid, s);
 }
 
 hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s) {
     hipLaunchKernelGGL(reduce_epilogue_kernel, dim3(grid), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, hipStream_t s) {
+    hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<unsigned>((N + 63) / 64),
+                                             static_cast<unsigned>((K + 63) / 64)),
+                       dim3(256), 0, s, W, Wt, K, N);
     return hipGetLastError();
 }
 
@@ -465,7 +546,7 @@ hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hi
 template <int MODE, int BK>
 static int occ_t() {
     int n = 0;
-    const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK>);
+    const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK, false>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n, fn, kThreads,
             static_cast<size_t>(TileCfg<BK>::LDS_BYTES)) != hipSuccess)

@@ -5,13 +5,12 @@
 // The chunk scheduler is this library's form of the CoCoNet record's (LIT-735, "Key
 // takeaways", second bullet) overlap of the model-parallel MatMul with the AllReduce
 // that consumes it, "in chunks"; the autotuner is its "autotunes the schedule" (first
-// bullet).  The chunk-size trade-off it searches is the bucket-size one of the
-// overlap pages: small chunks pay per-launch latency, large ones leave the last chunk's
+// bullet).  The chunk-size trade-off it searches is the bucket-size one of the overlap
+// pages: small chunks pay per-launch latency, large ones leave the last chunk's
 // reduction exposed.
 #include "../../include/mmar.h"
 
 #include <algorithm>
-#include <chrono>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -48,9 +47,13 @@ int fail(int code, const std::string& msg) {
 struct Plan {
     int sched = MMAR_SCHED_PERSISTENT;
     int cm = 0, cn = 0, ring = 0;
+    int wmode = MMAR_W_AUTO;   // MMAR_W_DIRECT or MMAR_W_PRETRANSPOSE once resolved
 };
 
 constexpr int kMaxRing = 8;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
 struct DevState {
     int id = -1;
@@ -62,7 +65,7 @@ struct DevState {
     void* ws = nullptr;
     size_t ws_bytes = 0;
     hipStream_t side = nullptr;
-    hipEvent_t ev_entry = nullptr, ev_side_done = nullptr;
+    hipEvent_t ev_side_done = nullptr;
     hipEvent_t ev_ws_free = nullptr;  // recorded after the last use of the library workspace
     hipEvent_t ev_gemm[kMaxRing] = {}, ev_red[kMaxRing] = {};
 };
@@ -98,6 +101,15 @@ int check_chunk(const Shape& s, int32_t cm, int32_t cn) {
         return fail(MMAR_EINVAL, "chunk_m must be a multiple of 32 dividing M");
     if (cn != 0 && (cn % 32 != 0 || s.N % cn != 0))
         return fail(MMAR_EINVAL, "chunk_n must be a multiple of 32 dividing N");
+    return MMAR_OK;
+}
+
+int check_sched(int32_t sched, int32_t ring, int32_t wmode) {
+    if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_PERSISTENT)
+        return fail(MMAR_EINVAL, "unknown schedule");
+    if (ring < 0 || ring > kMaxRing) return fail(MMAR_EINVAL, "ring must be in [0, 8]");
+    if (wmode < MMAR_W_AUTO || wmode > MMAR_W_PRETRANSPOSE)
+        return fail(MMAR_EINVAL, "unknown weight mode");
     return MMAR_OK;
 }
 
@@ -187,7 +199,6 @@ int ensure_workspace(DevState* st, size_t bytes) {
 int ensure_streams(DevState* st) {
     if (st->side) return MMAR_OK;
     MMAR_HIP(hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking));
-    MMAR_HIP(hipEventCreateWithFlags(&st->ev_entry, hipEventDisableTiming));
     MMAR_HIP(hipEventCreateWithFlags(&st->ev_side_done, hipEventDisableTiming));
     for (int i = 0; i < kMaxRing; ++i) {
         MMAR_HIP(hipEventCreateWithFlags(&st->ev_gemm[i], hipEventDisableTiming));
@@ -198,20 +209,27 @@ int ensure_streams(DevState* st) {
 }
 
 // ------------------------------------------------------------------ plans
+// Reading W [K, N] with the in-kernel LDS transpose costs some LDS time on every K step;
+// transposing W once per call costs 4 K N bytes of memory traffic and a launch.  On the
+// measured shapes the in-kernel read wins (the autotuner can still pick the other).
+int default_wmode(const Shape&) { return MMAR_W_DIRECT; }
+
 Plan default_plan(const Shape& s) {
     Plan p;
     p.sched = MMAR_SCHED_PERSISTENT;
     p.cm = static_cast<int>(s.M);
     p.cn = static_cast<int>(s.N);
     p.ring = 0;
+    p.wmode = default_wmode(s);
     return p;
 }
 
-// Fill in zero chunk sizes / ring for a schedule.
+// Fill in zero chunk sizes, ring and weight mode.
 Plan resolve(const Shape& s, Plan p) {
+    if (p.sched == MMAR_SCHED_AUTO) p.sched = MMAR_SCHED_PERSISTENT;
     if (p.sched == MMAR_SCHED_STREAMS) {
         if (p.cm == 0) {
-            // about 8 chunks of whole rows by default, each a multiple of 256 rows if possible
+            // about 8 chunks of whole rows by default
             int64_t cm = s.M;
             for (int64_t c : {s.M / 8, s.M / 4, s.M / 2}) {
                 if (c >= 32 && c % 32 == 0 && s.M % c == 0) {
@@ -229,15 +247,27 @@ Plan resolve(const Shape& s, Plan p) {
         if (p.cn == 0) p.cn = static_cast<int>(s.N);
         p.ring = p.sched == MMAR_SCHED_SEQUENTIAL ? 1 : 0;
     }
+    if (p.wmode == MMAR_W_AUTO) p.wmode = default_wmode(s);
     return p;
 }
 
-size_t ws_bytes_for(const Shape& s, const Plan& p) {
+// Workspace layout: [W^T (pre-transposed weight) | partial ring], each part 256-aligned.
+size_t wt_bytes_for(const Shape& s, const Plan& p, bool w_given_t) {
+    return (p.wmode == MMAR_W_PRETRANSPOSE && !w_given_t)
+               ? align_up(static_cast<size_t>(s.K) * static_cast<size_t>(s.N) * 2)
+               : 0;
+}
+
+size_t ring_bytes_for(const Shape& s, const Plan& p) {
     const size_t slot = static_cast<size_t>(s.P) * static_cast<size_t>(p.cm) *
                         static_cast<size_t>(p.cn) * sizeof(float);
-    if (p.sched == MMAR_SCHED_SEQUENTIAL) return slot;
-    if (p.sched == MMAR_SCHED_STREAMS) return slot * static_cast<size_t>(p.ring);
+    if (p.sched == MMAR_SCHED_SEQUENTIAL) return align_up(slot);
+    if (p.sched == MMAR_SCHED_STREAMS) return align_up(slot * static_cast<size_t>(p.ring));
     return 0;
+}
+
+size_t ws_bytes_for(const Shape& s, const Plan& p, bool w_given_t) {
+    return wt_bytes_for(s, p, w_given_t) + ring_bytes_for(s, p);
 }
 
 void load_plan_cache_locked() {
@@ -251,16 +281,18 @@ void load_plan_cache_locked() {
     while (std::fgets(line, sizeof line, f)) {
         char arch[64] = {0};
         long long M, N, K;
-        int P, sched, cm, cn, ring;
+        int P, sched, cm, cn, ring, wmode;
         if (std::sscanf(line,
                         " {\"arch\": \"%63[^\"]\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
-                        "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d",
-                        arch, &M, &N, &K, &P, &sched, &cm, &cn, &ring) == 9) {
+                        "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d, "
+                        "\"w_mode\": %d",
+                        arch, &M, &N, &K, &P, &sched, &cm, &cn, &ring, &wmode) == 10) {
             Plan p;
             p.sched = sched;
             p.cm = cm;
             p.cn = cn;
             p.ring = ring;
+            p.wmode = wmode;
             g_plans[PlanKey(arch, M, N, K, P)] = p;
         }
     }
@@ -279,10 +311,11 @@ void save_plan_cache_locked() {
         const Plan& p = kv.second;
         std::fprintf(f,
                      " {\"arch\": \"%s\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
-                     "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d}%s\n",
+                     "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d, "
+                     "\"w_mode\": %d}%s\n",
                      std::get<0>(k).c_str(), (long long)std::get<1>(k), (long long)std::get<2>(k),
                      (long long)std::get<3>(k), std::get<4>(k), p.sched, p.cm, p.cn, p.ring,
-                     ++i < g_plans.size() ? "," : "");
+                     p.wmode, ++i < g_plans.size() ? "," : "");
     }
     std::fprintf(f, "]\n");
     std::fclose(f);
@@ -295,16 +328,36 @@ Plan lookup_plan(const DevState* st, const Shape& s) {
     return it == g_plans.end() ? default_plan(s) : it->second;
 }
 
+// Plan for a call: the cached / default plan (schedule AUTO) or the explicit arguments,
+// with non-zero chunk / ring arguments and a non-AUTO weight mode overriding.
+Plan plan_for(const DevState* st, const Shape& s, int32_t sched, int32_t cm, int32_t cn,
+              int32_t ring, int32_t wmode) {
+    Plan p;
+    if (sched == MMAR_SCHED_AUTO) {
+        p = lookup_plan(st, s);
+    } else {
+        p.sched = sched;
+        p.ring = ring;
+        p.wmode = MMAR_W_AUTO;
+    }
+    if (cm) p.cm = cm;
+    if (cn) p.cn = cn;
+    if (ring) p.ring = ring;
+    if (wmode != MMAR_W_AUTO) p.wmode = wmode;
+    return resolve(s, p);
+}
+
 // ------------------------------------------------------------------ runners
 struct Call {
     const uint16_t *X, *W, *bias, *residual;
     float* out;
     Shape s;
     DropParams drop;
+    bool w_t;   // W holds W^T [N, K]
 };
 
 // K step of the tile kernel: 64 when it divides K/P, else 32.  MMAR_FORCE_BK=32 selects
-// the 32-wide step (deeper X prefetch, twice the barriers) for measurements.
+// the 32-wide step for measurements.
 int bk_for(const Shape& s) {
     static const int forced = [] {
         const char* e = std::getenv("MMAR_FORCE_BK");
@@ -354,7 +407,7 @@ int run_persistent(const DevState* st, const Call& c, int mode, int cm, int cn, 
     const int64_t items =
         static_cast<int64_t>(c.s.M / cm) * (c.s.N / cn) * tiles_in(cm, cn);
     a.total_items = static_cast<int32_t>(items);
-    MMAR_HIP(mmar::launch_tile(mode, bk, a, grid_for(st, mode, bk, a.total_items), s));
+    MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, a, grid_for(st, mode, bk, a.total_items), s));
     return MMAR_OK;
 }
 
@@ -366,7 +419,7 @@ int launch_partials(const DevState* st, const Call& c, int rm0, int rn0, int cm,
     const int64_t items = static_cast<int64_t>(tiles_in(cm, cn)) * c.s.P;
     if (items >= (int64_t(1) << 31)) return fail(MMAR_EINVAL, "too many work items");
     a.total_items = static_cast<int32_t>(items);
-    MMAR_HIP(mmar::launch_tile(mmar::kModePartials, bk, a,
+    MMAR_HIP(mmar::launch_tile(mmar::kModePartials, bk, c.w_t, a,
                                grid_for(st, mmar::kModePartials, bk, a.total_items), s));
     return MMAR_OK;
 }
@@ -435,24 +488,47 @@ int run_chunked(DevState* st, const Call& c, const Plan& p, float* ws, hipStream
     return MMAR_OK;
 }
 
-int run_plan(DevState* st, const Call& c, const Plan& p, void* workspace, size_t ws_bytes,
-             hipStream_t s) {
-    if (p.sched == MMAR_SCHED_PERSISTENT)
-        return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s);
-    const size_t need = ws_bytes_for(c.s, p);
+// What a call runs: the fused block (any schedule), or the measurement paths that share
+// its kernels.
+enum RunKind { kRunFused = 0, kRunReduced = 1, kRunPartials = 2 };
+
+// Runs a plan with the workspace `ws` (at least ws_bytes_for bytes).
+int run_with_ws(DevState* st, Call c, const Plan& p, RunKind kind, char* ws, hipStream_t s) {
+    const size_t wt_bytes = wt_bytes_for(c.s, p, c.w_t);
+    if (wt_bytes) {
+        uint16_t* wt = reinterpret_cast<uint16_t*>(ws);
+        MMAR_HIP(mmar::launch_transpose(c.W, wt, c.s.K, c.s.N, s));
+        c.W = wt;
+        c.w_t = true;
+    }
+    if (kind == kRunReduced) return run_persistent(st, c, mmar::kModeReduced, p.cm, p.cn, s);
+    if (kind == kRunPartials)
+        return launch_partials(st, c, 0, 0, static_cast<int>(c.s.M), static_cast<int>(c.s.N),
+                               c.out, s);
+    if (p.sched == MMAR_SCHED_PERSISTENT) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s);
+    return run_chunked(st, c, p, reinterpret_cast<float*>(ws + wt_bytes), s);
+}
+
+// Runs a plan with the caller's workspace, or with the library's (serialized per device
+// and ordered after earlier calls that used it on any stream).
+int run_plan(DevState* st, const Call& c, const Plan& p, RunKind kind, void* workspace,
+             size_t ws_bytes, hipStream_t s) {
+    size_t need = wt_bytes_for(c.s, p, c.w_t);
+    if (kind == kRunFused) need += ring_bytes_for(c.s, p);
     if (workspace) {
         if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
             return fail(MMAR_EALIGN, "workspace is not 16-byte aligned");
         if (ws_bytes < need)
             return fail(MMAR_ENOMEM, "workspace too small: need " + std::to_string(need) + " bytes");
-        return run_chunked(st, c, p, static_cast<float*>(workspace), s);
+        return run_with_ws(st, c, p, kind, static_cast<char*>(workspace), s);
     }
+    if (need == 0) return run_with_ws(st, c, p, kind, nullptr, s);
     std::lock_guard<std::mutex> lk(st->mu);
     int rc = ensure_workspace(st, need);
     if (rc) return rc;
     if (!st->ev_ws_free) MMAR_HIP(hipEventCreateWithFlags(&st->ev_ws_free, hipEventDisableTiming));
     else MMAR_HIP(hipStreamWaitEvent(s, st->ev_ws_free, 0));  // an earlier call on another stream
-    rc = run_chunked(st, c, p, static_cast<float*>(st->ws), s);
+    rc = run_with_ws(st, c, p, kind, static_cast<char*>(st->ws), s);
     if (rc) return rc;
     MMAR_HIP(hipEventRecord(st->ev_ws_free, s));
     return MMAR_OK;
@@ -482,36 +558,26 @@ int check_call(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
     c->residual = residual;
     c->out = out;
     c->s = s;
+    c->w_t = false;
     return MMAR_OK;
 }
 
-int fused_impl(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+int fused_impl(const uint16_t* X, const uint16_t* W, bool w_t, const uint16_t* bias,
                const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                int32_t P, float p_drop, uint64_t seed, int32_t sched, int32_t chunk_m,
-               int32_t chunk_n, int32_t ring, void* workspace, size_t ws_bytes,
+               int32_t chunk_n, int32_t ring, int32_t wmode, void* workspace, size_t ws_bytes,
                void* stream) {
     g_err.clear();
     Call c;
     const Shape s{M, N, K, P};
     int rc = check_call(X, W, bias, residual, out, s, p_drop, seed, chunk_m, chunk_n, &c);
     if (rc) return rc;
-    if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_PERSISTENT)
-        return fail(MMAR_EINVAL, "unknown schedule");
-    if (ring < 0 || ring > kMaxRing) return fail(MMAR_EINVAL, "ring must be in [0, 8]");
+    if ((rc = check_sched(sched, ring, wmode))) return rc;
+    c.w_t = w_t;
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
-    Plan p;
-    if (sched == MMAR_SCHED_AUTO) {
-        p = lookup_plan(st, s);
-    } else {
-        p.sched = sched;
-        p.ring = ring;
-    }
-    if (chunk_m) p.cm = chunk_m;
-    if (chunk_n) p.cn = chunk_n;
-    if (sched != MMAR_SCHED_AUTO && ring) p.ring = ring;
-    p = resolve(s, p);
-    return run_plan(st, c, p, workspace, ws_bytes, static_cast<hipStream_t>(stream));
+    const Plan p = plan_for(st, s, sched, chunk_m, chunk_n, ring, wmode);
+    return run_plan(st, c, p, kRunFused, workspace, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ autotuner
@@ -520,11 +586,11 @@ int time_plan(DevState* st, const Call& c, const Plan& p, hipStream_t s, float* 
     MMAR_HIP(hipEventCreate(&e0));
     MMAR_HIP(hipEventCreate(&e1));
     int rc = MMAR_OK;
-    for (int i = 0; i < 2 && !rc; ++i) rc = run_plan(st, c, p, nullptr, 0, s);
+    for (int i = 0; i < 2 && !rc; ++i) rc = run_plan(st, c, p, kRunFused, nullptr, 0, s);
     std::vector<float> t;
     for (int i = 0; i < 5 && !rc; ++i) {
         if (hipEventRecord(e0, s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
-        if (!rc) rc = run_plan(st, c, p, nullptr, 0, s);
+        if (!rc) rc = run_plan(st, c, p, kRunFused, nullptr, 0, s);
         if (!rc && hipEventRecord(e1, s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
         if (!rc && hipEventSynchronize(e1) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventSynchronize");
         float ms = 0;
@@ -559,20 +625,24 @@ int mmar_fused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                void* stream) {
-    return fused_impl(X, W, bias, residual, out, M, N, K, P, p_drop, seed, MMAR_SCHED_AUTO,
-                      chunk_m, chunk_n, 0, nullptr, 0, stream);
+    return fused_impl(X, W, false, bias, residual, out, M, N, K, P, p_drop, seed,
+                      MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_AUTO, nullptr, 0, stream);
+}
+
+int mmar_fused_nt(const uint16_t* X, const uint16_t* Wt, const uint16_t* bias,
+                  const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                  int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
+                  void* stream) {
+    return fused_impl(X, Wt, true, bias, residual, out, M, N, K, P, p_drop, seed,
+                      MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_DIRECT, nullptr, 0, stream);
 }
 
 size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, int32_t P,
-                            int32_t chunk_m, int32_t chunk_n, int32_t ring) {
+                            int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode) {
     g_err.clear();
     const Shape s{M, N, K, P};
-    if (check_shape(s) || check_chunk(s, chunk_m, chunk_n)) return 0;
-    if (schedule < MMAR_SCHED_AUTO || schedule > MMAR_SCHED_PERSISTENT || ring < 0 ||
-        ring > kMaxRing) {
-        fail(MMAR_EINVAL, "bad schedule or ring");
+    if (check_shape(s) || check_chunk(s, chunk_m, chunk_n) || check_sched(schedule, ring, w_mode))
         return 0;
-    }
     Plan p;
     if (schedule == MMAR_SCHED_AUTO) {
         std::lock_guard<std::mutex> lk(g_mu);
@@ -590,28 +660,44 @@ size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, i
     } else {
         p.sched = schedule;
         p.ring = ring;
+        p.wmode = MMAR_W_AUTO;
     }
     if (chunk_m) p.cm = chunk_m;
     if (chunk_n) p.cn = chunk_n;
-    if (schedule != MMAR_SCHED_AUTO && ring) p.ring = ring;
-    return ws_bytes_for(s, resolve(s, p));
+    if (ring) p.ring = ring;
+    if (w_mode != MMAR_W_AUTO) p.wmode = w_mode;
+    return ws_bytes_for(s, resolve(s, p), false);
 }
 
 int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                   int32_t P, float p_drop, uint64_t seed, int32_t schedule, int32_t chunk_m,
-                  int32_t chunk_n, int32_t ring, void* workspace, size_t ws_bytes,
-                  void* stream) {
-    return fused_impl(X, W, bias, residual, out, M, N, K, P, p_drop, seed, schedule, chunk_m,
-                      chunk_n, ring, workspace, ws_bytes, stream);
+                  int32_t chunk_n, int32_t ring, int32_t w_mode, void* workspace,
+                  size_t ws_bytes, void* stream) {
+    return fused_impl(X, W, false, bias, residual, out, M, N, K, P, p_drop, seed, schedule,
+                      chunk_m, chunk_n, ring, w_mode, workspace, ws_bytes, stream);
 }
 
 int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                     const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                     int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                     void* stream) {
-    return fused_impl(X, W, bias, residual, out, M, N, K, P, p_drop, seed,
-                      MMAR_SCHED_SEQUENTIAL, chunk_m, chunk_n, 0, nullptr, 0, stream);
+    return fused_impl(X, W, false, bias, residual, out, M, N, K, P, p_drop, seed,
+                      MMAR_SCHED_SEQUENTIAL, chunk_m, chunk_n, 0, MMAR_W_AUTO, nullptr, 0, stream);
+}
+
+int mmar_transpose_weight(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, void* stream) {
+    g_err.clear();
+    int rc;
+    if (K <= 0 || N <= 0 || K % 32 || N % 32 || K * N >= (int64_t(1) << 31))
+        return fail(MMAR_EINVAL, "K and N must be positive multiples of 32 with K N < 2^31");
+    if ((rc = check_ptr(W, "W")) || (rc = check_ptr(Wt, "Wt"))) return rc;
+    if (overlaps(W, static_cast<size_t>(K * N) * 2, Wt, static_cast<size_t>(K * N) * 2))
+        return fail(MMAR_EINVAL, "Wt overlaps W");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    MMAR_HIP(mmar::launch_transpose(W, Wt, K, N, static_cast<hipStream_t>(stream)));
+    return MMAR_OK;
 }
 
 int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M, int64_t N,
@@ -630,9 +716,13 @@ int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M
     c.W = W;
     c.out = T_out;
     c.s = s;
-    return run_persistent(st, c, mmar::kModeReduced, chunk_m ? chunk_m : static_cast<int>(M),
-                          chunk_n ? chunk_n : static_cast<int>(N),
-                          static_cast<hipStream_t>(stream));
+    Plan p = plan_for(st, s, MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_AUTO);
+    if (p.sched != MMAR_SCHED_PERSISTENT) {   // the GEMM of the persistent path
+        p.sched = MMAR_SCHED_PERSISTENT;
+        p.cm = chunk_m ? chunk_m : static_cast<int>(M);
+        p.cn = chunk_n ? chunk_n : static_cast<int>(N);
+    }
+    return run_plan(st, c, p, kRunReduced, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
 int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, int64_t M,
@@ -650,9 +740,10 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
     std::memset(&c, 0, sizeof c);
     c.X = X;
     c.W = W;
+    c.out = partials;
     c.s = s;
-    return launch_partials(st, c, 0, 0, static_cast<int>(M), static_cast<int>(N), partials,
-                           static_cast<hipStream_t>(stream));
+    const Plan p = plan_for(st, s, MMAR_SCHED_AUTO, 0, 0, 0, MMAR_W_AUTO);
+    return run_plan(st, c, p, kRunPartials, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
 int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
@@ -674,14 +765,13 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
 }
 
 int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
-                  int32_t chunk_m, int32_t chunk_n, int32_t ring) {
+                  int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode) {
     g_err.clear();
     const Shape s{M, N, K, P};
     int rc;
-    if ((rc = check_shape(s)) || (rc = check_chunk(s, chunk_m, chunk_n))) return rc;
-    if (schedule < MMAR_SCHED_AUTO || schedule > MMAR_SCHED_PERSISTENT || ring < 0 ||
-        ring > kMaxRing)
-        return fail(MMAR_EINVAL, "bad schedule or ring");
+    if ((rc = check_shape(s)) || (rc = check_chunk(s, chunk_m, chunk_n)) ||
+        (rc = check_sched(schedule, ring, w_mode)))
+        return rc;
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     std::lock_guard<std::mutex> lk(g_mu);
@@ -696,17 +786,19 @@ int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
     p.cm = chunk_m;
     p.cn = chunk_n;
     p.ring = ring;
+    p.wmode = w_mode;
     g_plans[key] = resolve(s, p);
     return MMAR_OK;
 }
 
 int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
-                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring) {
+                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring, int32_t* w_mode) {
     g_err.clear();
     const Shape s{M, N, K, P};
     int rc;
     if ((rc = check_shape(s))) return rc;
-    if (!schedule || !chunk_m || !chunk_n || !ring) return fail(MMAR_EINVAL, "NULL output pointer");
+    if (!schedule || !chunk_m || !chunk_n || !ring || !w_mode)
+        return fail(MMAR_EINVAL, "NULL output pointer");
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     const Plan p = resolve(s, lookup_plan(st, s));
@@ -714,6 +806,7 @@ int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
     *chunk_m = p.cm;
     *chunk_n = p.cn;
     *ring = p.ring;
+    *w_mode = p.wmode;
     return MMAR_OK;
 }
 
@@ -727,14 +820,16 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
 
     // candidate plans
     std::vector<Plan> cands;
-    for (int cm : divisors32(M, {1, 2, 4}))
-        for (int cn : divisors32(N, {1, 2})) {
-            Plan p;
-            p.sched = MMAR_SCHED_PERSISTENT;
-            p.cm = cm;
-            p.cn = cn;
-            cands.push_back(p);
-        }
+    for (int wm : {MMAR_W_DIRECT, MMAR_W_PRETRANSPOSE})
+        for (int cm : divisors32(M, {1, 2, 4}))
+            for (int cn : divisors32(N, {1, 2})) {
+                Plan p;
+                p.sched = MMAR_SCHED_PERSISTENT;
+                p.cm = cm;
+                p.cn = cn;
+                p.wmode = wm;
+                cands.push_back(p);
+            }
     if (flags & 1u) {
         for (int cm : divisors32(M, {2, 4, 8, 16}))
             for (int r : {2, 3}) {
@@ -743,10 +838,12 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
                 p.cm = cm;
                 p.cn = static_cast<int>(N);
                 p.ring = r;
+                p.wmode = default_wmode(s);
                 cands.push_back(p);
             }
         Plan p;
         p.sched = MMAR_SCHED_SEQUENTIAL;
+        p.wmode = default_wmode(s);
         cands.push_back(p);
     }
 
@@ -784,6 +881,7 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
     c.residual = r;
     c.out = o;
     c.s = s;
+    c.w_t = false;
     drop_params(0.1f, 1234, &c.drop);
 
     Plan best;
@@ -811,7 +909,7 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
 
 const char* mmar_last_error(void) { return g_err.c_str(); }
 
-const char* mmar_version(void) { return "mmar 0.1.0 gfx950"; }
+const char* mmar_version(void) { return "mmar 0.2.0 gfx950"; }
 
 int mmar_release(void) {
     g_err.clear();
@@ -825,13 +923,12 @@ int mmar_release(void) {
         (void)hipDeviceSynchronize();
         if (st->ws) (void)hipFree(st->ws);
         st->ws = nullptr;
+        st->ws_bytes = 0;
         if (st->ev_ws_free) (void)hipEventDestroy(st->ev_ws_free);
         st->ev_ws_free = nullptr;
-        st->ws_bytes = 0;
         if (st->side) {
             (void)hipStreamDestroy(st->side);
             st->side = nullptr;
-            (void)hipEventDestroy(st->ev_entry);
             (void)hipEventDestroy(st->ev_side_done);
             for (int i = 0; i < kMaxRing; ++i) {
                 (void)hipEventDestroy(st->ev_gemm[i]);

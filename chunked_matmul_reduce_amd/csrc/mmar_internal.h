@@ -27,7 +27,7 @@ struct DropParams {
 // RN) and each chunk into BM x BN tiles visited in chunk order.
 struct TileArgs {
     const uint16_t* X;   // [M, K] bf16 bits
-    const uint16_t* W;   // [K, N] bf16 bits
+    const uint16_t* W;   // [K, N] bf16 bits, or W^T [N, K] for the transposed-W kernel
     const uint16_t* bias;
     const uint16_t* residual;
     float* out;          // kModeFused / kModeReduced: [M, N]
@@ -55,8 +55,10 @@ constexpr int kBM = 256;   // output rows per tile (4 waves x 64)
 constexpr int kBN = 128;   // output columns per tile
 constexpr int kThreads = 256;
 
-// Launchers (kernels.hip).  bk is 64 or 32 (the K step; it must divide Ks).
-hipError_t launch_tile(int mode, int bk, const TileArgs& a, int grid, hipStream_t s);
+// Launchers (kernels.hip).  bk is 64 or 32 (the K step; it must divide Ks).  wt: a.W
+// holds W^T [N, K] instead of W [K, N].
+hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, hipStream_t s);
+hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, hipStream_t s);
 hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s);
 // Workgroups of the tile kernel that fit on one CU at once (0 on error).

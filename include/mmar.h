@@ -34,7 +34,14 @@
  *
  * Layouts.  X [M,K], W [K,N], residual [M,N] row-major, contiguous, bf16 bit patterns
  * (uint16); bias [N] bf16 bits; out [M,N] row-major fp32.  All tensor pointers are
- * DEVICE pointers on the current HIP device.
+ * DEVICE pointers on the current HIP device.  mmar_fused_nt takes the weight
+ * transposed, W^T [N,K] row-major (the layout of a Linear layer's weight).
+ *
+ * Weight modes.  The tile kernel needs each lane's MFMA operand as 8 consecutive k of one
+ * column of W.  MMAR_W_DIRECT reads W [K,N] as given and transposes fragments with the LDS
+ * transpose read; MMAR_W_PRETRANSPOSE first writes W^T [N,K] into the workspace
+ * (4 K N bytes of memory traffic) and then reads both operands with plain 16-byte LDS
+ * reads.  Both produce identical bits.
  *
  * Preconditions (checked; violations return MMAR_EINVAL before any device work and
  * leave `out` untouched): M, N, K > 0; 1 <= P <= 4096; K % P == 0; (K/P) % 32 == 0;
@@ -45,8 +52,8 @@
  *
  * Ownership.  The caller owns every tensor and keeps it alive until the stream has
  * passed the call; the library never frees or retains caller memory.  The library owns
- * a per-device workspace, a second stream and events, created on first use and freed by
- * mmar_release().  Calls that use the library workspace are serialized per device by a
+ * a per-device workspace (partial-product ring, pre-transposed weight), a second stream
+ * and events, created on first use and freed by mmar_release().  Calls that use the library workspace are serialized per device by a
  * mutex; with a caller workspace (mmar_fused_ex) calls are re-entrant.
  *
  * Errors.  Every int-returning call returns MMAR_OK (0) or a negative code; details of
@@ -85,6 +92,8 @@ enum {
     MMAR_SCHED_PERSISTENT = 3
 };
 
+enum { MMAR_W_AUTO = -1, MMAR_W_DIRECT = 0, MMAR_W_PRETRANSPOSE = 1 };
+
 /* The fused block with the library's schedule for this shape: the plan set by
  * mmar_set_plan or found by mmar_autotune, else the persistent schedule.  chunk_m /
  * chunk_n override the plan's chunk when non-zero.  Uses the library workspace. */
@@ -93,11 +102,22 @@ int mmar_fused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                void* stream);
 
-/* Workspace bytes a schedule needs (0 for MMAR_SCHED_PERSISTENT; for AUTO, the plan's).
- * ring = number of chunk slots for MMAR_SCHED_STREAMS (0 = the default, 2).
- * Returns 0 and sets the last error on invalid sizes. */
+/* The same block with the weight given transposed, Wt = W^T [N,K] row-major (the layout of
+ * a Linear layer's weight); no transpose is needed.  Same plan, same bits as mmar_fused
+ * on W = Wt^T. */
+int mmar_fused_nt(const uint16_t* X, const uint16_t* Wt, const uint16_t* bias,
+                  const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                  int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
+                  void* stream);
+
+/* Workspace bytes a plan needs: K N 2 (256-aligned) for MMAR_W_PRETRANSPOSE, plus the
+ * partial-product ring for MMAR_SCHED_SEQUENTIAL (P chunk_m chunk_n 4) and
+ * MMAR_SCHED_STREAMS (ring times that).  schedule AUTO: the plan mmar_fused would use
+ * (with non-zero chunk / ring and non-AUTO w_mode arguments overriding).  ring = number of
+ * chunk slots for MMAR_SCHED_STREAMS (0 = the default, 2).  Returns 0 and sets the last
+ * error on invalid arguments. */
 size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, int32_t P,
-                            int32_t chunk_m, int32_t chunk_n, int32_t ring);
+                            int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode);
 
 /* The fused block with every choice explicit.  workspace == NULL: the library's
  * workspace is used (serialized per device); otherwise `workspace` (device memory,
@@ -107,8 +127,8 @@ size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, i
 int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                   int32_t P, float p_drop, uint64_t seed, int32_t schedule, int32_t chunk_m,
-                  int32_t chunk_n, int32_t ring, void* workspace, size_t ws_bytes,
-                  void* stream);
+                  int32_t chunk_n, int32_t ring, int32_t w_mode, void* workspace,
+                  size_t ws_bytes, void* stream);
 
 /* MMAR_SCHED_SEQUENTIAL with the library workspace: the "same fusion without overlap"
  * comparison point of the CoCoNet record ("Key takeaways", second bullet). */
@@ -117,14 +137,19 @@ int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                     int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                     void* stream);
 
-/* Measurement entry point: the persistent kernel with the epilogue removed.  Writes the
- * reduced sum T = S_0 + ... + S_{P-1} (fp32, fixed order) to T_out [M,N]; the same
- * MFMA sequence as mmar_fused, so T_out + epilogue reproduces its bits. */
+/* W [K,N] -> W^T [N,K] (bf16 bits), for callers that keep the transposed weight and call
+ * mmar_fused_nt.  K, N positive multiples of 32; Wt must not overlap W. */
+int mmar_transpose_weight(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, void* stream);
+
+/* Measurement entry point: the persistent kernel with the epilogue removed, with the plan's
+ * weight mode (its transpose included).  Writes the reduced sum T = S_0 + ... + S_{P-1}
+ * (fp32, fixed order) to T_out [M,N]; the same MFMA sequence as mmar_fused, so T_out +
+ * epilogue reproduces its bits.  Uses the library workspace for a pre-transposed W. */
 int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M, int64_t N,
                    int64_t K, int32_t P, int32_t chunk_m, int32_t chunk_n, void* stream);
 
 /* Measurement entry point: the P per-slice partials S_p, fp32, written to
- * partials [P][M][N] (each slice accumulated from zero). */
+ * partials [P][M][N] (each slice accumulated from zero), with the plan's weight mode. */
 int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, int64_t M,
                        int64_t N, int64_t K, int32_t P, void* stream);
 
@@ -136,7 +161,7 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
                               int32_t P, float p_drop, uint64_t seed, void* stream);
 
 /* The autotuner (the page's "autotunes the schedule", "Key takeaways", first bullet):
- * times candidate {schedule, chunk, ring} plans for this shape on library-owned
+ * times candidate {schedule, chunk, ring, weight mode} plans for this shape on library-owned
  * buffers, keeps the fastest in the plan cache (also written to the JSON file named by
  * the MMAR_PLAN_CACHE environment variable, if set) and returns MMAR_OK.  flags: bit 0
  * = also try MMAR_SCHED_STREAMS and MMAR_SCHED_SEQUENTIAL plans.  Synchronizes the
@@ -144,12 +169,13 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
 int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags);
 
 /* Set / read the plan used by mmar_fused for this shape on the current device.
- * schedule is one of MMAR_SCHED_*, AUTO clears the entry.  mmar_get_plan writes the
- * plan that mmar_fused would use (the default when none is set). */
+ * schedule is one of MMAR_SCHED_*, AUTO clears the entry; w_mode one of MMAR_W_*.
+ * mmar_get_plan writes the plan that mmar_fused would use (the default when none is
+ * set: persistent, whole-output chunk, MMAR_W_DIRECT). */
 int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
-                  int32_t chunk_m, int32_t chunk_n, int32_t ring);
+                  int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode);
 int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
-                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring);
+                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring, int32_t* w_mode);
 
 /* Text of the last error on the calling thread ("" if none).  Valid until the next
  * call on this thread. */

@@ -56,19 +56,32 @@ def test_other_entry_points_validate():
     assert L.mmar_reduce_epilogue_only(FAKE, FAKE, FAKE, FAKE, 64, 64, 2, 2.0, 0, None) == mmar.EINVAL
     assert L.mmar_reduce_epilogue_only(FAKE, FAKE, FAKE, FAKE, 60, 64, 2, 0.1, 0, None) == mmar.EINVAL
     assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 7,
-                           0, 0, 0, None, 0, None) == mmar.EINVAL
+                           0, 0, 0, -1, None, 0, None) == mmar.EINVAL
     assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 2,
-                           0, 0, 9, None, 0, None) == mmar.EINVAL
-    assert L.mmar_set_plan(64, 256, 256, 4, 9, 0, 0, 0) == mmar.EINVAL
+                           0, 0, 9, -1, None, 0, None) == mmar.EINVAL
+    assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 2,
+                           0, 0, 0, 5, None, 0, None) == mmar.EINVAL
+    assert "weight mode" in mmar.last_error()
+    assert L.mmar_fused_nt(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 250, 4, 0.1, 0, 0,
+                           0, None) == mmar.EINVAL
+    assert L.mmar_transpose_weight(FAKE, FAKE, 64, 64, None) == mmar.EINVAL   # overlap
+    assert L.mmar_transpose_weight(FAKE, FAKE * 64, 60, 64, None) == mmar.EINVAL
+    assert L.mmar_set_plan(64, 256, 256, 4, 9, 0, 0, 0, -1) == mmar.EINVAL
     assert L.mmar_autotune(64, 256, 250, 4, 0) == mmar.EINVAL
 
 
 def test_workspace_bytes():
+    wt = 12288 * 3072 * 2   # pre-transposed weight of the 8192-row block
     assert mmar.workspace_bytes("persistent", 8192, 3072, 12288, 16) == 0
+    assert mmar.workspace_bytes("persistent", 8192, 3072, 12288, 16, w_mode="pretranspose") == wt
     assert mmar.workspace_bytes("sequential", 8192, 3072, 12288, 16) == 4 * 16 * 8192 * 3072
+    assert mmar.workspace_bytes("sequential", 8192, 3072, 12288, 16, w_mode="pretranspose") == \
+        4 * 16 * 8192 * 3072 + wt
     assert mmar.workspace_bytes("sequential", 64, 256, 256, 4, chunk=(32, 64)) == 4 * 4 * 32 * 64
     assert mmar.workspace_bytes("streams", 1024, 512, 256, 4, chunk=(256, 512), ring=3) == \
         3 * 4 * 4 * 256 * 512
+    assert mmar.workspace_bytes("streams", 1024, 512, 256, 4, chunk=(256, 512), ring=3,
+                                w_mode="pretranspose") == 3 * 4 * 4 * 256 * 512 + 256 * 512 * 2
     with pytest.raises(mmar.MmarError):
         mmar.workspace_bytes("streams", 1024, 512, 250, 4)
 

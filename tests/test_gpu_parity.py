@@ -28,12 +28,12 @@ def _to_dev(inp):
     return {k: dev(inp[k], torch) for k in ("X", "W", "bias", "residual")}
 
 
-def _run(d, P, p, seed, sched="auto", chunk=(0, 0), ring=0):
-    if sched == "auto":
+def _run(d, P, p, seed, sched="auto", chunk=(0, 0), ring=0, w_mode="auto"):
+    if sched == "auto" and w_mode == "auto":
         out = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, p, seed, chunk=chunk)
     else:
         out = mmar.fused_ex(d["X"], d["W"], d["bias"], d["residual"], P, p, seed, sched,
-                            chunk=chunk, ring=ring)
+                            chunk=chunk, ring=ring, w_mode=w_mode)
     torch.cuda.synchronize()
     return host(out)
 
@@ -70,10 +70,11 @@ def test_tiny_all_schedules_chunks_bit_identical():
     outs = {}
     for sched in SCHEDS:
         for chunk in [(32, 64), (64, 64), (32, 256), (64, 256), (0, 0)]:
-            out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk)
-            outs[(sched, chunk)] = out
-            print(sched, chunk, "max rel err", _check_block(inp, out), flush=True)
-    ref = f32_bits(outs[("persistent", (32, 64))])
+            for wm in ("direct", "pretranspose"):
+                out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, w_mode=wm)
+                outs[(sched, chunk, wm)] = out
+                print(sched, chunk, wm, "max rel err", _check_block(inp, out), flush=True)
+    ref = f32_bits(outs[("persistent", (32, 64), "direct")])
     for k, o in outs.items():
         assert np.array_equal(f32_bits(o), ref), k
     keep = _mask_readout(w.M, w.N, w.K, w.P, inp["p_drop"], w.seed, chunk=w.chunk)
@@ -99,11 +100,19 @@ def test_ragged_shapes_against_oracle(M, K, N, P):
     ref = None
     for sched in SCHEDS:
         for chunk in [(0, 0), (32, 32), (M // 2 if (M // 2) % 32 == 0 else M, N)]:
-            out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk)
-            _check_block(inp, out)
-            if ref is None:
-                ref = f32_bits(out)
-            assert np.array_equal(f32_bits(out), ref), (sched, chunk)
+            for wm in ("direct", "pretranspose"):
+                out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk, w_mode=wm)
+                _check_block(inp, out)
+                if ref is None:
+                    ref = f32_bits(out)
+                assert np.array_equal(f32_bits(out), ref), (sched, chunk, wm)
+    # the weight given transposed (Linear layout)
+    Wt = mmar.transpose_weight(d["W"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(Wt.view(torch.int16)), inp["W"].T.view(np.int16))
+    out = mmar.fused_nt(d["X"], Wt, d["bias"], d["residual"], P, inp["p_drop"], inp["seed"])
+    torch.cuda.synchronize()
+    assert np.array_equal(f32_bits(host(out)), ref)
 
 
 # ---------------------------------------------------------------- full-size workloads
@@ -135,12 +144,15 @@ def test_full_size_schedule_invariance():
     w = WORKLOADS["gpt2_attn"]
     inp = make_inputs("gpt2_attn")
     d = _to_dev(inp)
-    ref = f32_bits(_run(d, w.P, inp["p_drop"], w.seed, "persistent"))
-    for sched, chunk, ring in [("persistent", (w.M // 2, w.N // 2), 0), ("persistent", (1024, 3072), 0),
-                               ("streams", (1024, w.N), 2), ("streams", (2048, 1536), 3),
-                               ("sequential", (0, 0), 0)]:
-        out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, ring)
-        assert np.array_equal(f32_bits(out), ref), (sched, chunk, ring)
+    ref = f32_bits(_run(d, w.P, inp["p_drop"], w.seed, "persistent", w_mode="direct"))
+    for sched, chunk, ring, wm in [("persistent", (0, 0), 0, "pretranspose"),
+                                   ("persistent", (w.M // 2, w.N // 2), 0, "direct"),
+                                   ("persistent", (1024, 3072), 0, "pretranspose"),
+                                   ("streams", (1024, w.N), 2, "direct"),
+                                   ("streams", (2048, 1536), 3, "pretranspose"),
+                                   ("sequential", (0, 0), 0, "direct")]:
+        out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, ring, w_mode=wm)
+        assert np.array_equal(f32_bits(out), ref), (sched, chunk, ring, wm)
 
 
 # ---------------------------------------------------------------- structure pins
@@ -218,7 +230,7 @@ def test_gemm_only_and_partials_compose_to_fused():
     M, K, N, P = 512, 1024, 384, 4
     inp = make_random_inputs(M, K, N, seed=13)
     d = _to_dev(inp)
-    fused = _run(d, P, 0.1, 3, "persistent")
+    fused = _run(d, P, 0.1, 3, "persistent", w_mode="direct")
     T = mmar.gemm_only(d["X"], d["W"], P)
     o1 = mmar.reduce_epilogue_only(T[None], d["bias"], d["residual"], 0.1, 3)
     parts = mmar.gemm_partials(d["X"], d["W"], P)
@@ -239,13 +251,14 @@ def test_repeat_caller_workspace_and_stream():
     d = _to_dev(inp)
     ref = f32_bits(_run(d, P, 0.1, 9, "persistent"))
     assert np.array_equal(f32_bits(_run(d, P, 0.1, 9, "persistent")), ref)
-    for sched, ring in [("sequential", 0), ("streams", 2), ("streams", 3)]:
-        nbytes = mmar.workspace_bytes(sched, M, N, K, P, chunk=(128, N), ring=ring)
+    for sched, ring, wm in [("sequential", 0, "direct"), ("streams", 2, "direct"),
+                            ("streams", 3, "pretranspose"), ("persistent", 0, "pretranspose")]:
+        nbytes = mmar.workspace_bytes(sched, M, N, K, P, chunk=(128, N), ring=ring, w_mode=wm)
         ws = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
         out = mmar.fused_ex(d["X"], d["W"], d["bias"], d["residual"], P, 0.1, 9, sched,
-                            chunk=(128, N), ring=ring, workspace=ws)
+                            chunk=(128, N), ring=ring, w_mode=wm, workspace=ws)
         torch.cuda.synchronize()
-        assert np.array_equal(f32_bits(host(out)), ref), sched
+        assert np.array_equal(f32_bits(host(out)), ref), (sched, wm)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         out = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, 0.1, 9)
@@ -271,7 +284,7 @@ def test_invalid_arguments_leave_out_untouched():
     assert rc == mmar.EALIGN
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     rc = mmar.lib.mmar_fused_ex(*ptrs, out.data_ptr(), M, N, K, P, 0.1, 1, mmar.SCHED_SEQUENTIAL,
-                                0, 0, 0, small.data_ptr(), 16, None)
+                                0, 0, 0, mmar.W_DIRECT, small.data_ptr(), 16, None)
     assert rc == mmar.ENOMEM
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
@@ -286,8 +299,9 @@ def test_autotune_keeps_bits():
     plan = mmar.get_plan(M, N, K, P)
     print("tuned plan", plan, flush=True)
     assert np.array_equal(f32_bits(_run(d, P, 0.1, 4)), ref)
-    mmar.set_plan(M, N, K, P, "streams", chunk=(256, N), ring=2)
-    assert mmar.get_plan(M, N, K, P)["schedule"] == mmar.SCHED_STREAMS
+    mmar.set_plan(M, N, K, P, "streams", chunk=(256, N), ring=2, w_mode="pretranspose")
+    plan = mmar.get_plan(M, N, K, P)
+    assert plan["schedule"] == mmar.SCHED_STREAMS and plan["w_mode"] == mmar.W_PRETRANSPOSE
     assert np.array_equal(f32_bits(_run(d, P, 0.1, 4)), ref)
     mmar.set_plan(M, N, K, P, "auto")
     assert mmar.get_plan(M, N, K, P)["schedule"] == mmar.SCHED_PERSISTENT
