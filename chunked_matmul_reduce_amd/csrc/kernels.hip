@@ -53,8 +53,12 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t hi0 = __umulhi(kM0, c0), lo0 = kM0 * c0;
-        const uint32_t hi1 = __umulhi(kM1, c2), lo1 = kM1 * c2;
+        // one 32 x 32 -> 64-bit multiply per product (v_mad_u64_u32), not a separate
+        // high and low multiply
+        const uint64_t p0 = static_cast<uint64_t>(kM0) * c0;
+        const uint64_t p1 = static_cast<uint64_t>(kM1) * c2;
+        const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+        const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
         const uint32_t n0 = hi1 ^ c1 ^ k0;
         const uint32_t n2 = hi0 ^ c3 ^ k1;
         c0 = n0;
@@ -108,8 +112,9 @@ struct TileCfg {
     static constexpr int RW = BM / WM, CW = BN / WN;    // rows / columns of a wave
     static constexpr int MB = RW / 32, NB = CW / 32;    // 32 x 32 MFMA blocks of a wave
     static constexpr int KS = BK / 16;                  // MFMA k steps per K step
-    static constexpr int XSTAGES = 3;                   // X ring depth (copies 2 steps ahead)
-    static constexpr int WSTAGES = 4;                   // W ring depth (one more: early barrier)
+    static constexpr int LEAD = BK == 64 ? 2 : 5;       // copies run LEAD K steps ahead
+    static constexpr int XSTAGES = LEAD + 1;            // X ring depth
+    static constexpr int WSTAGES = LEAD + 2;            // W ring depth (one more: early barrier)
     static constexpr int XS = BM * BK;                  // elements of an X stage [BM][BK]
     static constexpr int WS = BK * BN;                  // elements of a W stage [BK][BN]
     static constexpr int CPR = BK / 8;                  // 16-byte chunks per X row
@@ -306,18 +311,18 @@ void tile_kernel(TileArgs a) {
             }
         };
         // Step-boundary handshake for K step t: this wave's copies of t are done (only the
-        // copies of the following step may remain) and the barrier makes every wave's
-        // copies of t visible; it also shows that every wave finished step t-2, whose W
-        // stage the copies issued next (for step t+2) reuse.
+        // copies of the LEAD - 1 following steps may remain) and the barrier makes every
+        // wave's copies of t visible; it also shows that every wave finished step t-2, whose
+        // W stage the copies issued next (for step t + LEAD) reuse.
         auto handshake = [&]() {
-            MMAR_WAIT_VM(C::DMA);
+            MMAR_WAIT_VM((C::LEAD - 1) * C::DMA);
             wg_barrier();
         };
 
 #pragma unroll
-        for (int i = 0; i < C::DMA; ++i) copy(0, i);
+        for (int d = 0; d < C::LEAD; ++d)
 #pragma unroll
-        for (int i = 0; i < C::DMA; ++i) copy(min(1, last), i);
+            for (int i = 0; i < C::DMA; ++i) copy(min(d, last), i);
         handshake();
 
         // fragments are double-buffered: k step s of any K step uses buffer s % 2 (KS is
@@ -332,9 +337,9 @@ void tile_kernel(TileArgs a) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) S[nb][mb] = f32x16{};
           for (int j = 0; j < sps; ++j, ++st) {
-            // copies of step st+2 (the last steps re-copy the last one: identical bytes,
+            // copies of step st+LEAD (the last steps re-copy the last one: identical bytes,
             // no branch), spread over the MFMAs of k steps 0 .. KS-2
-            const int st2 = min(st + 2, last);
+            const int st2 = min(st + C::LEAD, last);
             // the 8 MFMAs of one k step, with copies c0 .. c1-1 issued between them (all of
             // them: the caller passes c1 - c0 <= DMA)
             auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1) {
@@ -384,37 +389,67 @@ void tile_kernel(TileArgs a) {
         wg_barrier();   // every wave is done with the LDS ring before the next item's copies
 
         // Store / epilogue.  Lane holds rows RW wm + 32 mb + l32 and, in registers
-        // 4g..4g+3 of block nb, columns CW wn + 32 nb + 8 g + 4 h + 0..3.
+        // 4g..4g+3 of block nb, columns CW wn + 32 nb + 8 g + 4 h + 0..3.  A ragged tile
+        // holds whole 32 x 32 blocks (rows and cols are multiples of 32); blocks outside
+        // it are neither loaded nor stored.  The fused mode loads every bias and residual
+        // value it needs first, so the loads are in flight together (and under the Philox
+        // arithmetic) instead of one load latency per output group.
+        auto col_ok = [&](int nb) { return C::CW * wn + 32 * nb < cols; };
+        auto row_ok = [&](int mb) { return C::RW * wm + 32 * mb < rows; };
+        if constexpr (MODE == kModeFused) {
+            uint2 bb[NB][4], rb[NB][4][MB];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int nl = C::CW * wn + 32 * nb + 8 * g + 4 * h;
-                if (nl >= cols) continue;
-                const int64_t n = n0 + nl;
-                uint2 bb = make_uint2(0u, 0u);
-                if (MODE == kModeFused) bb = *reinterpret_cast<const uint2*>(a.bias + n);
+                for (int g = 0; g < 4; ++g) {
+                    // clamped into the tile: an outside block reads a valid address
+                    const int nl = min(C::CW * wn + 32 * nb, cols - 32) + 8 * g + 4 * h;
+                    bb[nb][g] = *reinterpret_cast<const uint2*>(a.bias + n0 + nl);
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const int ml = C::RW * wm + 32 * mb + l32;
-                    if (ml >= rows) continue;
-                    const int64_t m = m0 + ml;
-                    const f32x16& acc = (MODE == kModePartials) ? S[nb][mb] : T[nb][mb];
-                    const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
-                                                 acc[4 * g + 3]);
-                    if (MODE == kModeFused) {
-                        const int64_t e = m * a.N + n;
-                        const uint2 rb = *reinterpret_cast<const uint2*>(a.residual + e);
-                        *reinterpret_cast<float4*>(a.out + e) = epilogue4(v, bb, rb, e, a.drop);
-                    } else if (MODE == kModeReduced) {
-                        *reinterpret_cast<float4*>(a.out + m * a.N + n) = v;
-                    } else {
-                        float* dst = a.ws + static_cast<int64_t>(p_lo) * a.RM * a.RN +
-                                     (m - a.rm0) * a.RN + (n - a.rn0);
-                        *reinterpret_cast<float4*>(dst) = v;
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const int ml = min(C::RW * wm + 32 * mb, rows - 32) + l32;
+                        rb[nb][g][mb] = *reinterpret_cast<const uint2*>(
+                            a.residual + (static_cast<int64_t>(m0) + ml) * a.N + n0 + nl);
                     }
                 }
-            }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        if (!col_ok(nb) || !row_ok(mb)) continue;
+                        const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
+                        const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
+                        const f32x16& acc = T[nb][mb];
+                        const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
+                                                     acc[4 * g + 3]);
+                        const int64_t e = m * a.N + n;
+                        *reinterpret_cast<float4*>(a.out + e) =
+                            epilogue4(v, bb[nb][g], rb[nb][g][mb], e, a.drop);
+                    }
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        if (!col_ok(nb) || !row_ok(mb)) continue;
+                        const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
+                        const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
+                        const f32x16& acc = (MODE == kModePartials) ? S[nb][mb] : T[nb][mb];
+                        const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
+                                                     acc[4 * g + 3]);
+                        if (MODE == kModeReduced) {
+                            *reinterpret_cast<float4*>(a.out + m * a.N + n) = v;
+                        } else {
+                            float* dst = a.ws + static_cast<int64_t>(p_lo) * a.RM * a.RN +
+                                         (m - a.rm0) * a.RN + (n - a.rn0);
+                            *reinterpret_cast<float4*>(dst) = v;
+                        }
+                    }
+        }
     }
 }
 
