@@ -1,6 +1,6 @@
 """Benchmark of the fused MatMul -> slice-reduce -> epilogue block on one MI355X.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload gpt2_mlp]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 50] [--workload gpt2_mlp]
 
 A step is one call of the whole block (all P slice GEMMs, the fixed-order slice
 reduction, bias + Philox dropout + residual) on one batch of seeded synthetic input
@@ -11,6 +11,9 @@ One JSON line on stdout: throughput in TFLOP/s (2*M*N*K per step), the roofline 
 dominant kernel (the persistent fused tile kernel, timed per launch with HIP events on
 the stream it runs on), the hidden fraction 1 - (T_fused - T_gemm_alone) / T_re_alone,
 and the oracle's CPU throughput on a bounded sample of the same workload.
+
+The default warm-up (50 steps, about 30 ms) takes the GPU past the clock transient of
+its first launches; the timed steps then run at the sustained clock.
 
 --only fused     time only the fused block (for rocprofv3 runs)
 --only copy      one plain 1 GiB device copy, the calibration point for HBM counters
@@ -88,8 +91,8 @@ def _cpu_baseline(inp, w, budget_s):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gpt2_mlp")
     ap.add_argument("--only", choices=["all", "fused", "copy"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=30.0)

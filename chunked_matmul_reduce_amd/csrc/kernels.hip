@@ -35,6 +35,8 @@
 //
 // No fused multiply-add anywhere in the epilogue (built with -ffp-contract=off and
 // written with explicit round-to-nearest add / multiply).
+#include <type_traits>
+
 #include "mmar_internal.h"
 
 namespace mmar {
@@ -59,8 +61,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
         const uint64_t p1 = static_cast<uint64_t>(kM1) * c2;
         const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
         const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
-        const uint32_t n0 = hi1 ^ c1 ^ k0;
-        const uint32_t n2 = hi0 ^ c3 ^ k1;
+        // three-input XORs, one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
+        const uint32_t n0 = __builtin_amdgcn_bitop3_b32(hi1, c1, k0, 0x96);
+        const uint32_t n2 = __builtin_amdgcn_bitop3_b32(hi0, c3, k1, 0x96);
         c0 = n0;
         c1 = lo1;
         c2 = n2;
@@ -331,25 +334,26 @@ void tile_kernel(TileArgs a) {
         frags(0, 0, xa, wa);
 
         int st = 0;
-        for (int p = p_lo; p < p_hi; ++p) {
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) S[nb][mb] = f32x16{};
-          for (int j = 0; j < sps; ++j, ++st) {
+        // One K step (step st): KS k steps of 8 MFMAs, the copies of step st+LEAD between
+        // them, the step-boundary handshake before the last k step.  ZERO marks the first
+        // K step of a slice: its first k step gives the MFMAs a zero accumulator input,
+        // which starts the slice sums from zero without clearing any register.
+        auto kstep = [&](auto zero_tag) {
+            constexpr bool ZERO = decltype(zero_tag)::value;
             // copies of step st+LEAD (the last steps re-copy the last one: identical bytes,
             // no branch), spread over the MFMAs of k steps 0 .. KS-2
             const int st2 = min(st + C::LEAD, last);
             // the 8 MFMAs of one k step, with copies c0 .. c1-1 issued between them (all of
             // them: the caller passes c1 - c0 <= DMA)
-            auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1) {
+            auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1,
+                             bool zero) {
                 int c = c0;
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb) {
-                        S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[nb], xf[mb],
-                                                                            S[nb][mb], 0, 0, 0);
+                        S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            wf[nb], xf[mb], zero ? f32x16{} : S[nb][mb], 0, 0, 0);
                         // spread the copies evenly over the 8 MFMAs
                         const int upto = c0 + ((nb * MB + mb + 1) * (c1 - c0) + 7) / 8;
                         while (c < upto) {
@@ -364,18 +368,24 @@ void tile_kernel(TileArgs a) {
             for (int s = 0; s < KS; s += 2) {
                 // k step s (buffer a), prefetching s+1 into buffer b
                 frags(st, s + 1, xb2, wb2);
-                mfmas(xa, wa, min(s * CPS, C::DMA), min((s + 1) * CPS, C::DMA));
+                mfmas(xa, wa, min(s * CPS, C::DMA), min((s + 1) * CPS, C::DMA), ZERO && s == 0);
                 // k step s+1 (buffer b), prefetching s+2, or the next K step's first
                 if (s + 2 < KS) {
                     frags(st, s + 2, xa, wa);
-                    mfmas(xb2, wb2, min((s + 1) * CPS, C::DMA), min((s + 2) * CPS, C::DMA));
+                    mfmas(xb2, wb2, min((s + 1) * CPS, C::DMA), min((s + 2) * CPS, C::DMA),
+                          false);
                 } else {
                     handshake();
                     frags(min(st + 1, last), 0, xa, wa);
-                    mfmas(xb2, wb2, C::DMA, C::DMA);
+                    mfmas(xb2, wb2, C::DMA, C::DMA, false);
                 }
             }
-          }
+        };
+
+        for (int p = p_lo; p < p_hi; ++p) {
+          kstep(std::true_type{});
+          ++st;
+          for (int j = 1; j < sps; ++j, ++st) kstep(std::false_type{});
           if (MODE != kModePartials) {
               // T = 0 + S_0 (= S_0 exactly: an MFMA sum started from +0 is never -0),
               // then T + S_1, T + S_2, ... in fp32, round to nearest even
