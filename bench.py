@@ -10,7 +10,10 @@ M=8192, K=12288 split in P=16 slices, N=3072 (bf16 in, fp32 accumulate and out).
 One JSON line on stdout: throughput in TFLOP/s (2*M*N*K per step), the roofline of the
 dominant kernel (the persistent fused tile kernel, timed per launch with HIP events on
 the stream it runs on), the hidden fraction 1 - (T_fused - T_gemm_alone) / T_re_alone,
-and the oracle's CPU throughput on a bounded sample of the same workload.
+and the oracle's CPU throughput on a bounded sample of the same workload.  Comparison
+legs: the sequential schedule (same kernels, no overlap), the two-stream schedule, and
+the unfused path (one kernel per operation, mask materialized); their ratios to the
+fused time are the one-GPU analogues of the pages' block-level speedups.
 
 The default warm-up (50 steps, about 30 ms) takes the GPU past the clock transient of
 its first launches; the timed steps then run at the sustained clock.
@@ -189,6 +192,10 @@ def main():
         t_seq = _ev_time(torch, lambda: mmar.sequential(X, W, bias, res, P, p, seed, out=out), reps)[0]
         t_str = _ev_time(torch, lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "streams", out=out),
                          reps)[0]
+        mask = torch.empty((w.M, w.N), dtype=torch.uint8, device="cuda")
+        t_unf = _ev_time(torch, lambda: mmar.unfused(X, W, bias, res, P, p, seed, out=out, mask=mask),
+                         reps)[0]
+        del mask
         t_dir = _ev_time(torch, lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "persistent",
                                                       w_mode="direct", out=out), reps)[0]
         t_pre = _ev_time(torch, lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "persistent",
@@ -204,13 +211,14 @@ def main():
         result["times_us"] = {k: round(v * 1e3, 2) for k, v in
                               {"fused": t_fused, "gemm_alone": t_gemm, "partials_gemm": t_parts,
                                "re_alone": t_re, "epi_alone": t_epi, "sequential": t_seq,
-                               "streams": t_str, "persistent_w_direct": t_dir,
+                               "streams": t_str, "unfused": t_unf, "persistent_w_direct": t_dir,
                                "persistent_w_pretranspose": t_pre, "w_transpose": t_tr,
                                "persistent_w_given_transposed": t_nt}.items()}
         result["hidden_fraction"] = round(1.0 - (t_fused - t_gemm) / t_re, 4)
         result["hidden_fraction_epilogue"] = round(1.0 - (t_fused - t_gemm) / t_epi, 4)
         result["speedup_vs_sequential"] = round(t_seq / t_fused, 3)
         result["speedup_streams_vs_sequential"] = round(t_seq / t_str, 3)
+        result["speedup_vs_unfused"] = round(t_unf / t_fused, 3)
         result["re_alone_GBps"] = round(re_bytes / (t_re * 1e-3) / 1e9, 1)
         result["epi_alone_GBps"] = round(epi_bytes / (t_epi * 1e-3) / 1e9, 1)
 

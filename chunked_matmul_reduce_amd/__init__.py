@@ -41,6 +41,7 @@ _SIGNATURES = {
                                      _I32, _I32, _I32, _P, _SZ, _P]),
     "mmar_transpose_weight": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "mmar_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
+    "mmar_unfused": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _P]),
     "mmar_gemm_only": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "mmar_gemm_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "mmar_reduce_epilogue_only": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _F, _U64, _P]),
@@ -243,6 +244,28 @@ def sequential(X, W, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, st
                                  out.data_ptr(), M, N, K, int(P), float(p_drop),
                                  int(seed) & (2 ** 64 - 1), int(chunk[0]), int(chunk[1]),
                                  _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def unfused(X, W, bias, residual, P, p_drop, seed, out=None, mask=None, stream=None):
+    """mmar_unfused: the block one kernel per operation (partials GEMM, reduction, bias add,
+    dropout, residual add).  `mask`: a uint8 [M, N] GPU tensor that receives the keep mask
+    (1 = kept), or None.  Returns out."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, P)
+    out = _out(out, (M, N), X)
+    mp = None
+    if mask is not None:
+        if mask.device.type != "cuda" or mask.dtype != torch.uint8 or tuple(mask.shape) != (M, N) \
+                or not mask.is_contiguous():
+            raise ValueError(f"mask must be a contiguous uint8 GPU tensor of shape {(M, N)}")
+        mp = mask.data_ptr()
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_unfused(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), _bits(bias, "bias", (N,)),
+                              _bits(residual, "residual", (M, N)), out.data_ptr(), mp, M, N, K,
+                              int(P), float(p_drop), int(seed) & (2 ** 64 - 1),
+                              _stream(X.device, stream))
     _check(rc)
     return out
 

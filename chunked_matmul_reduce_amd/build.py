@@ -17,8 +17,10 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmmar.so")
-SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "mmar.cpp")]
-HEADERS = [os.path.join(PKG, "csrc", "mmar_internal.h"), os.path.join(ROOT, "include", "mmar.h")]
+SOURCES = [os.path.join(PKG, "csrc", "kernels.hip"), os.path.join(PKG, "csrc", "unfused.hip"),
+           os.path.join(PKG, "csrc", "mmar.cpp")]
+HEADERS = [os.path.join(PKG, "csrc", "mmar_internal.h"), os.path.join(PKG, "csrc", "device_common.h"),
+           os.path.join(ROOT, "include", "mmar.h")]
 ARCH = "gfx950"
 
 

@@ -37,45 +37,13 @@
 // written with explicit round-to-nearest add / multiply).
 #include <type_traits>
 
+#include "device_common.h"
 #include "mmar_internal.h"
 
 namespace mmar {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-// ------------------------------------------------------------------ Philox4x32-10
-// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11.
-// Round: the 64-bit products M0*c0 and M1*c2 split into high / low words; new counter
-// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key is bumped by the Weyl increments
-// between rounds.
-__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
-                                               uint32_t c3, uint32_t k0, uint32_t k1) {
-    constexpr uint32_t kM0 = 0xD2511F53u, kM1 = 0xCD9E8D57u;
-    constexpr uint32_t kW0 = 0x9E3779B9u, kW1 = 0xBB67AE85u;
-#pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        // one 32 x 32 -> 64-bit multiply per product (v_mad_u64_u32), not a separate
-        // high and low multiply
-        const uint64_t p0 = static_cast<uint64_t>(kM0) * c0;
-        const uint64_t p1 = static_cast<uint64_t>(kM1) * c2;
-        const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
-        const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
-        // three-input XORs, one v_bitop3_b32 each (truth table 0x96 = a ^ b ^ c)
-        const uint32_t n0 = __builtin_amdgcn_bitop3_b32(hi1, c1, k0, 0x96);
-        const uint32_t n2 = __builtin_amdgcn_bitop3_b32(hi0, c3, k1, 0x96);
-        c0 = n0;
-        c1 = lo1;
-        c2 = n2;
-        c3 = lo0;
-        k0 += kW0;
-        k1 += kW1;
-    }
-    return make_uint4(c0, c1, c2, c3);
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 __device__ __forceinline__ float epi1(float t, float b, float r, uint32_t word,
                                       const DropParams& d) {

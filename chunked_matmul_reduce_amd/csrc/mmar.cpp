@@ -4,8 +4,8 @@
 //
 // The chunk scheduler is this library's form of the CoCoNet record's (LIT-735, "Key
 // takeaways", second bullet) overlap of the model-parallel MatMul with the AllReduce
-// that consumes it, "in chunks"; the autotuner is its "autotunes the schedule" (first
-// bullet).  The chunk-size trade-off it searches is the bucket-size one of the overlap
+// that consumes it, chunk by chunk; the autotuner stands for CoCoNet's automatic search
+// over schedules (first bullet).  The chunk-size trade-off it searches is the bucket-size one of the overlap
 // pages: small chunks pay per-launch latency, large ones leave the last chunk's
 // reduction exposed.
 #include "../../include/mmar.h"
@@ -744,6 +744,40 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
     c.s = s;
     const Plan p = plan_for(st, s, MMAR_SCHED_AUTO, 0, 0, 0, MMAR_W_AUTO);
     return run_plan(st, c, p, kRunPartials, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+int mmar_unfused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                 const uint16_t* residual, float* out, uint8_t* mask, int64_t M, int64_t N,
+                 int64_t K, int32_t P, float p_drop, uint64_t seed, void* stream) {
+    g_err.clear();
+    Call c;
+    int rc = check_call(X, W, bias, residual, out, Shape{M, N, K, P}, p_drop, seed, 0, 0, &c);
+    if (rc) return rc;
+    if (mask) {
+        if ((rc = check_ptr(mask, "mask"))) return rc;
+        if (overlaps(mask, static_cast<size_t>(M * N), out, static_cast<size_t>(M * N) * 4))
+            return fail(MMAR_EINVAL, "mask overlaps out");
+    }
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const size_t part_bytes = align_up(static_cast<size_t>(P) * M * N * 4);
+    const size_t need = part_bytes + (mask ? 0 : align_up(static_cast<size_t>(M * N)));
+    std::lock_guard<std::mutex> lk(st->mu);
+    if ((rc = ensure_workspace(st, need))) return rc;
+    if (!st->ev_ws_free) MMAR_HIP(hipEventCreateWithFlags(&st->ev_ws_free, hipEventDisableTiming));
+    else MMAR_HIP(hipStreamWaitEvent(s, st->ev_ws_free, 0));
+    float* ws = static_cast<float*>(st->ws);
+    uint8_t* m = mask ? mask : static_cast<uint8_t*>(st->ws) + part_bytes;
+    c.w_t = false;
+    rc = launch_partials(st, c, 0, 0, static_cast<int>(M), static_cast<int>(N), ws, s);
+    if (rc) return rc;
+    const int64_t groups = M * N / 4;
+    const int grid = static_cast<int>(std::max<int64_t>(
+        1, std::min<int64_t>((groups + 255) / 256, static_cast<int64_t>(st->cus) * 8)));
+    MMAR_HIP(mmar::launch_unfused_tail(ws, ws, bias, residual, out, m, M, N, P, c.drop, grid, s));
+    MMAR_HIP(hipEventRecord(st->ev_ws_free, s));
+    return MMAR_OK;
 }
 
 int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,

@@ -61,6 +61,12 @@ hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, h
 hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, hipStream_t s);
 hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s);
+// The unfused tail (unfused.hip): sum of the P partials ws [P][M][N] into T (may alias ws),
+// then bias add, dropout (keep bytes to mask [M][N]) and residual add into out, each its
+// own kernel on stream s.
+hipError_t launch_unfused_tail(const float* ws, float* T, const uint16_t* bias,
+                               const uint16_t* residual, float* out, uint8_t* mask, int64_t M,
+                               int64_t N, int32_t P, const DropParams& d, int grid, hipStream_t s);
 // Workgroups of the tile kernel that fit on one CU at once (0 on error).
 int tile_occupancy(int mode, int bk);
 int reduce_occupancy();

@@ -22,7 +22,8 @@
  * does not depend on chunking or on the schedule, and neither do the output bits:
  * every schedule below produces identical bytes.
  *
- * Schedules (the chunk scheduler; the page's "overlapping the two in chunks"):
+ * Schedules (the chunk scheduler: the MatMul and the reduction overlapped chunk by chunk,
+ * as the CoCoNet record's second key takeaway describes):
  *   MMAR_SCHED_SEQUENTIAL  GEMM of a chunk's P partials into a workspace, then the
  *                          reduce+epilogue of that chunk, on one stream, no overlap.
  *   MMAR_SCHED_STREAMS     the same two kernels, the reduce+epilogue of chunk c on a
@@ -130,8 +131,9 @@ int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   int32_t chunk_n, int32_t ring, int32_t w_mode, void* workspace,
                   size_t ws_bytes, void* stream);
 
-/* MMAR_SCHED_SEQUENTIAL with the library workspace: the "same fusion without overlap"
- * comparison point of the CoCoNet record ("Key takeaways", second bullet). */
+/* MMAR_SCHED_SEQUENTIAL with the library workspace: the comparison point of the CoCoNet
+ * record that fuses the same work but does not overlap it ("Key takeaways", second
+ * bullet). */
 int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                     const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                     int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
@@ -153,6 +155,18 @@ int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M
 int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, int64_t M,
                        int64_t N, int64_t K, int32_t P, void* stream);
 
+/* Comparison entry point: the same block computed unfused, one kernel per operation, the
+ * way frameworks that call computation and communication as separate library kernels run
+ * it (the baseline the CoCoNet record compares against, "Key takeaways", first and second
+ * bullets): the P slice GEMMs write all partials to a workspace, a reduction kernel sums
+ * them left to right, then separate bias-add, dropout and residual-add kernels.  The
+ * dropout kernel writes the keep mask as bytes (1 = kept) to `mask` [M][N] (uint8,
+ * device; NULL: to the library workspace).  Same arguments, preconditions and output bits
+ * as mmar_fused; uses the library workspace, 4*P*M*N (+ M*N without `mask`) bytes. */
+int mmar_unfused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                 const uint16_t* residual, float* out, uint8_t* mask, int64_t M, int64_t N,
+                 int64_t K, int32_t P, float p_drop, uint64_t seed, void* stream);
+
 /* The slice reduction plus epilogue alone, over P materialized fp32 partials
  * [P][M][N]: T = S_0 + S_1 + ... (fixed order), then the bias, dropout and residual
  * epilogue.  With P = 1 it is the epilogue alone over a materialized T. */
@@ -160,7 +174,8 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
                               const uint16_t* residual, float* out, int64_t M, int64_t N,
                               int32_t P, float p_drop, uint64_t seed, void* stream);
 
-/* The autotuner (the page's "autotunes the schedule", "Key takeaways", first bullet):
+/* The autotuner (CoCoNet picks its schedules by automatic search; "Key takeaways", first
+ * bullet):
  * times candidate {schedule, chunk, ring, weight mode} plans for this shape on library-owned
  * buffers, keeps the fastest in the plan cache (also written to the JSON file named by
  * the MMAR_PLAN_CACHE environment variable, if set) and returns MMAR_OK.  flags: bit 0

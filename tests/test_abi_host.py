@@ -66,6 +66,16 @@ def test_other_entry_points_validate():
                            0, None) == mmar.EINVAL
     assert L.mmar_transpose_weight(FAKE, FAKE, 64, 64, None) == mmar.EINVAL   # overlap
     assert L.mmar_transpose_weight(FAKE, FAKE * 64, 60, 64, None) == mmar.EINVAL
+    U = L.mmar_unfused
+    assert U(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, None, 64, 256, 250, 4, 0.1, 0, None) == \
+        mmar.EINVAL   # P does not divide K
+    assert U(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, FAKE * 128 + 4, 64, 256, 256, 4, 0.1, 0,
+             None) == mmar.EALIGN   # mask misaligned
+    assert U(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, FAKE * 64 + 4096, 64, 256, 256, 4, 0.1, 0,
+             None) == mmar.EINVAL   # mask overlaps out
+    assert "overlaps" in mmar.last_error()
+    assert U(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, None, 64, 256, 256, 4, 1.5, 0, None) == \
+        mmar.EINVAL   # p outside [0, 1]
     assert L.mmar_set_plan(64, 256, 256, 4, 9, 0, 0, 0, -1) == mmar.EINVAL
     assert L.mmar_autotune(64, 256, 250, 4, 0) == mmar.EINVAL
 

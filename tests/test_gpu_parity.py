@@ -305,3 +305,40 @@ def test_autotune_keeps_bits():
     assert np.array_equal(f32_bits(_run(d, P, 0.1, 4)), ref)
     mmar.set_plan(M, N, K, P, "auto")
     assert mmar.get_plan(M, N, K, P)["schedule"] == mmar.SCHED_PERSISTENT
+
+
+# ---------------------------------------------------------------- unfused comparison path
+UNFUSED_CASES = ["tiny", (288, 480, 160, 5), (1056, 2048, 544, 8), "gpt2_attn"]
+
+
+@pytest.mark.parametrize("case", UNFUSED_CASES, ids=str)
+def test_unfused_matches_fused_bits_and_oracle_mask(case):
+    """One kernel per operation gives the fused path's bits; its materialized mask is the
+    oracle's keep mask, byte for byte."""
+    if isinstance(case, str):
+        w = WORKLOADS[case]
+        inp = make_inputs(case)
+        M, K, N, P, p, seed = w.M, w.K, w.N, w.P, inp["p_drop"], w.seed
+    else:
+        M, K, N, P = case
+        p, seed = np.float32(0.3), 12345 + M
+        inp = make_random_inputs(M, K, N, seed=7 * M + N)
+        inp.update(M=M, K=K, N=N, P=P, p_drop=p, seed=seed)
+    print("unfused", case, flush=True)
+    d = _to_dev(inp)
+    mask = torch.full((M, N), 7, dtype=torch.uint8, device="cuda")
+    out_u = mmar.unfused(d["X"], d["W"], d["bias"], d["residual"], P, p, seed, mask=mask)
+    out_f = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, p, seed)
+    torch.cuda.synchronize()
+    ou = host(out_u)
+    assert np.array_equal(f32_bits(ou), f32_bits(host(out_f)))
+    m = host(mask)
+    assert set(np.unique(m).tolist()) <= {0, 1}
+    assert np.array_equal(m.astype(bool), oracle.keep_mask(M, N, p, seed))
+    if M * N <= (1 << 20):
+        _check_block(inp, ou)
+    for pp in (0.0, 1.0):   # no mask buffer; the two edge values of p
+        u = mmar.unfused(d["X"], d["W"], d["bias"], d["residual"], P, pp, seed)
+        f = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, pp, seed)
+        torch.cuda.synchronize()
+        assert np.array_equal(f32_bits(host(u)), f32_bits(host(f))), pp
