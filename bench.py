@@ -52,6 +52,19 @@ def _ev_time(torch, fn, reps):
     return times[len(times) // 2], sum(times) / len(times)
 
 
+TILE_KERNEL_SOURCES = ("tile_kernel.hip", "device_common.h", "mmar_internal.h")
+
+
+def tile_kernel_sha():
+    """sha256 over the sources that define the fused tile kernel (its counters are valid
+    only for this exact code)."""
+    h = hashlib.sha256()
+    for name in TILE_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "chunked_matmul_reduce_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def _traffic(kernel_sha):
     """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
     path = os.path.join(ROOT, "profiles", "traffic_tile_kernel_fused_gpt2_mlp.json")
@@ -60,7 +73,7 @@ def _traffic(kernel_sha):
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("kernels_hip_sha256") != kernel_sha:
+    if d.get("tile_kernel_sources_sha256") != kernel_sha:
         return None
     return d.get("traffic_bytes_per_launch")
 
@@ -167,8 +180,7 @@ def main():
                             "chunk": list(plan["chunk"]), "ring": plan["ring"],
                             "w_mode": {0: "direct", 1: "pretranspose"}[plan["w_mode"]]}},
     }
-    with open(os.path.join(ROOT, "chunked_matmul_reduce_amd", "csrc", "kernels.hip"), "rb") as f:
-        ksha = hashlib.sha256(f.read()).hexdigest()
+    ksha = tile_kernel_sha()
     achieved = flops / (kernel_ms * 1e-3) / 1e12
     result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                           "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),

@@ -1,9 +1,13 @@
-// Device helpers shared by the gfx950 kernels (kernels.hip, unfused.hip): the Philox
-// generator of the dropout mask and bf16 unpacking.
+// Device helpers shared by the gfx950 kernels (tile_kernel.hip, reduce_kernels.hip,
+// unfused.hip): the Philox generator of the dropout mask, bf16 unpacking and the fused
+// epilogue (bias add, inverted dropout, residual add; round to nearest even, no fused
+// multiply-add).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "mmar_internal.h"
 
 namespace mmar {
 
@@ -39,5 +43,27 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float epi1(float t, float b, float r, uint32_t word,
+                                      const DropParams& d) {
+    const float v = __fadd_rn(t, b);
+    const float y = __fmul_rn(v, d.scale);
+    const bool keep = (d.drop_all == 0u) && (word >= d.thr);
+    return keep ? __fadd_rn(r, y) : r;
+}
+
+// Epilogue of four consecutive outputs starting at linear index e (e % 4 == 0).
+__device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int64_t e,
+                                            const DropParams& d) {
+    const uint64_t g = static_cast<uint64_t>(e) >> 2;
+    const uint4 w = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32),
+                                  0u, 0u, d.key0, d.key1);
+    float4 o;
+    o.x = epi1(t.x, bf16_lo(bias.x), bf16_lo(res.x), w.x, d);
+    o.y = epi1(t.y, bf16_hi(bias.x), bf16_hi(res.x), w.y, d);
+    o.z = epi1(t.z, bf16_lo(bias.y), bf16_lo(res.y), w.z, d);
+    o.w = epi1(t.w, bf16_hi(bias.y), bf16_hi(res.y), w.w, d);
+    return o;
+}
 
 }  // namespace mmar

@@ -1,25 +1,31 @@
-// gfx950 kernels of the fused MatMul -> slice-reduce -> epilogue block.
+// The tile kernel of the fused MatMul -> slice-reduce -> epilogue block (gfx950).
 //
 // The block (CoCoNet record LIT-735, "Key takeaways": the model-parallel MatMul whose
 // partial products an AllReduce sums, overlapped in chunks, with pointwise work fused
 // into the collective) folded onto one GPU: P K-slices stand in for P ranks, and a
 // fixed-order fp32 sum of the slice partials stands in for the AllReduce.
 //
-// Tile kernel.  A 256-thread workgroup (4 waves) owns a 256 x 128 output tile.  Wave w
+// A 256-thread workgroup (4 waves, one per SIMD) owns a 256 x 128 output tile; wave w
 // owns rows [64w, 64w+64) and all 128 columns, as 2 x 4 blocks of 32 x 32 computed with
 // v_mfma_f32_32x32x16_bf16.  The MFMA computes the transposed block (W^T in the A slot,
 // X in the B slot), so that a lane's accumulator holds one output row and, per group of
 // four registers, four consecutive columns: exactly one Philox group, one 8-byte bias /
 // residual load and one 16-byte fp32 store, with no cross-lane exchange.
-//   * X is not shared between waves (each wave owns its rows), so it goes straight from
-//     HBM/L2 into registers, double-buffered one K step ahead.
-//   * W is shared by the 4 waves: each K step's [BK x 128] tile is loaded with 8-byte
-//     row loads, transposed in registers to k-contiguous 16-byte rows and written to a
-//     double-buffered LDS tile [128][BK + 8] (the 16-byte pad makes the MFMA operand
-//     reads bank-conflict free); one barrier per K step.
-//   * Slice semantics: S (the current slice's accumulator) starts from zero at every
-//     slice boundary; at the end of a slice T = S (first slice) or T = T + S (fp32, RNE),
-//     so the partials are reduced in the fixed order p = 0..P-1 without leaving registers.
+//   * Staging: global_load_lds_dwordx4 copies (HBM/L2 -> LDS, no register round trip)
+//     into a ring of X stages [256][BK] and a ring of W stages [BK][128] (W^T [128][BK]
+//     when W is given transposed), LEAD K steps ahead; 16-byte chunks are XOR-swizzled
+//     so the copies and the operand reads are bank-conflict free.  W [K, N] operands are
+//     read with the LDS transpose read ds_read_b64_tr_b16, everything else with 16-byte
+//     reads.
+//   * Pipelining: the copies of step t+LEAD are spread between the MFMAs of step t; one
+//     handshake per K step (this wave's copies done, then a workgroup barrier) placed
+//     before the last k step, so the first operand fragments of step t+1 are read under
+//     the last MFMAs of step t.  All waits are explicit vector-memory waits: no compiler
+//     fence drains the copies in flight.
+//   * Slice semantics: S starts every slice from zero (the first MFMA of a slice takes a
+//     zero accumulator input); after the slice T = T + S (fp32, round to nearest even; T
+//     starts at +0, and 0 + S_0 = S_0), so the partials are reduced in the fixed order
+//     p = 0..P-1 without leaving registers.
 //   * Modes: kModeFused applies bias + Philox dropout + residual to T and stores fp32
 //     out; kModeReduced stores T; kModePartials computes one slice per work item and
 //     stores S_p to a workspace.  All three share the same MFMA sequence, so partials
@@ -29,9 +35,8 @@
 //     workgroup ids are remapped so the 32 workgroups resident on one XCD (ids are
 //     dealt round-robin over the 8 XCDs) take 32 consecutive items and share their
 //     X rows and W columns in that XCD's L2.
-//
-// Reduce+epilogue kernel.  One thread per group of four consecutive outputs: P 16-byte
-// partial loads summed left to right, then the same epilogue.  HBM-bound.
+//   * Epilogue: every bias and residual load of the tile is issued before the first
+//     Philox block is computed, so the load latency is paid once per tile.
 //
 // No fused multiply-add anywhere in the epilogue (built with -ffp-contract=off and
 // written with explicit round-to-nearest add / multiply).
@@ -44,28 +49,6 @@ namespace mmar {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-__device__ __forceinline__ float epi1(float t, float b, float r, uint32_t word,
-                                      const DropParams& d) {
-    const float v = __fadd_rn(t, b);
-    const float y = __fmul_rn(v, d.scale);
-    const bool keep = (d.drop_all == 0u) && (word >= d.thr);
-    return keep ? __fadd_rn(r, y) : r;
-}
-
-// Epilogue of four consecutive outputs starting at linear index e (e % 4 == 0).
-__device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int64_t e,
-                                            const DropParams& d) {
-    const uint64_t g = static_cast<uint64_t>(e) >> 2;
-    const uint4 w = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32),
-                                  0u, 0u, d.key0, d.key1);
-    float4 o;
-    o.x = epi1(t.x, bf16_lo(bias.x), bf16_lo(res.x), w.x, d);
-    o.y = epi1(t.y, bf16_hi(bias.x), bf16_hi(res.x), w.y, d);
-    o.z = epi1(t.z, bf16_lo(bias.y), bf16_lo(res.y), w.z, d);
-    o.w = epi1(t.w, bf16_hi(bias.y), bf16_hi(res.y), w.w, d);
-    return o;
-}
 
 // ------------------------------------------------------------------ tile kernel
 #define MMAR_LDS __attribute__((address_space(3)))
@@ -431,78 +414,6 @@ void tile_kernel(TileArgs a) {
     }
 }
 
-// ------------------------------------------------------------------ reduce + epilogue
-__global__ __launch_bounds__(256) void reduce_epilogue_kernel(ReduceArgs a) {
-    const int groups_per_row = a.RN / 4;
-    const int total = a.RM * groups_per_row;
-    const int64_t plane = static_cast<int64_t>(a.RM) * a.RN;
-    for (int q = blockIdx.x * 256 + threadIdx.x; q < total; q += gridDim.x * 256) {
-        const int r = q / groups_per_row, c = (q - r * groups_per_row) * 4;
-        const float* src = a.ws + static_cast<int64_t>(r) * a.RN + c;
-        float4 t = *reinterpret_cast<const float4*>(src);
-        for (int p = 1; p < a.P; ++p) {
-            const float4 s = *reinterpret_cast<const float4*>(src + p * plane);
-            t.x = __fadd_rn(t.x, s.x);
-            t.y = __fadd_rn(t.y, s.y);
-            t.z = __fadd_rn(t.z, s.z);
-            t.w = __fadd_rn(t.w, s.w);
-        }
-        const int64_t e = static_cast<int64_t>(a.rm0 + r) * a.N + (a.rn0 + c);
-        const uint2 bb = *reinterpret_cast<const uint2*>(a.bias + a.rn0 + c);
-        const uint2 rb = *reinterpret_cast<const uint2*>(a.residual + e);
-        *reinterpret_cast<float4*>(a.out + e) = epilogue4(t, bb, rb, e, a.drop);
-    }
-}
-
-// ------------------------------------------------------------------ W -> W^T
-// [K, N] -> [N, K] bf16 through a padded 64 x 64 LDS tile: 16-byte coalesced loads of
-// W rows and 16-byte coalesced stores of W^T rows.  K and N are multiples of 8.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ W,
-                                                        uint16_t* __restrict__ Wt, int64_t K,
-                                                        int64_t N) {
-    __shared__ uint16_t tile[64][64 + 2];
-    const int64_t k0 = static_cast<int64_t>(blockIdx.y) * 64, n0 = static_cast<int64_t>(blockIdx.x) * 64;
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {   // 64 rows x 8 chunks of 8 elements
-        const int idx = t + 256 * r, row = idx / 8, ch = idx % 8;
-        const int64_t k = k0 + row, n = n0 + 8 * ch;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (k < K && n < N) v = *reinterpret_cast<const uint4*>(W + k * N + n);
-        const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tile[row][8 * ch + i] = e[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int idx = t + 256 * r, col = idx / 8, ch = idx % 8;
-        const int64_t n = n0 + col, k = k0 + 8 * ch;
-        if (n < N && k < K) {
-            uint16_t e[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) e[i] = tile[8 * ch + i][col];
-            *reinterpret_cast<uint4*>(Wt + n * K + k) = *reinterpret_cast<const uint4*>(e);
-        }
-    }
-}
-
-// ------------------------------------------------------------------ fill (tuner inputs)
-__global__ __launch_bounds__(256) void fill_bf16_kernel(uint16_t* p, int64_t n, uint32_t salt,
-                                                        float amp) {
-    for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += gridDim.x * 256ll) {
-        uint32_t x = static_cast<uint32_t>(i) * 0x9E3779B1u ^ salt ^ static_cast<uint32_t>(i >> 32);
-        x ^= x >> 16;
-        x *= 0x7FEB352Du;
-        x ^= x >> 15;
-        x *= 0x846CA68Bu;
-        x ^= x >> 16;
-        const float u = __fmul_rn(static_cast<float>(x >> 8), 1.0f / 16777216.0f);  // [0, 1)
-        const float v = __fmul_rn(__fsub_rn(__fmul_rn(u, 2.0f), 1.0f), amp);
-        p[i] = static_cast<uint16_t>(__float_as_uint(v) >> 16);
-    }
-}
-
 // ------------------------------------------------------------------ launchers
 template <int MODE, int BK, bool WT>
 static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
@@ -535,27 +446,6 @@ hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, h
     return wt ? launch_tile_w<true>(mode, bk, a, grid, s) : launch_tile_w<false>(mode, bk, a, grid, s);
 }
 
-hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s) {
-    hipLaunchKernelGGL(reduce_epilogue_kernel, dim3(grid), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, hipStream_t s) {
-    hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<unsigned>((N + 63) / 64),
-                                             static_cast<unsigned>((K + 63) / 64)),
-                       dim3(256), 0, s, W, Wt, K, N);
-    return hipGetLastError();
-}
-
-hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s) {
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 65536) blocks = 65536;
-    if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(fill_bf16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p,
-                       n, salt, amp);
-    return hipGetLastError();
-}
-
 template <int MODE, int BK>
 static int occ_t() {
     int n = 0;
@@ -576,14 +466,6 @@ int tile_occupancy(int mode, int bk) {
     if (mode == kModeFused) return occ_t<kModeFused, 32>();
     if (mode == kModeReduced) return occ_t<kModeReduced, 32>();
     return occ_t<kModePartials, 32>();
-}
-
-int reduce_occupancy() {
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reduce_epilogue_kernel, 256, 0) !=
-        hipSuccess)
-        return 0;
-    return n;
 }
 
 }  // namespace mmar
