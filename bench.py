@@ -13,7 +13,9 @@ the stream it runs on), the hidden fraction 1 - (T_fused - T_gemm_alone) / T_re_
 and the oracle's CPU throughput on a bounded sample of the same workload.  Comparison
 legs: the sequential schedule (same kernels, no overlap), the two-stream schedule, and
 the unfused path (one kernel per operation, mask materialized); their ratios to the
-fused time are the one-GPU analogues of the pages' block-level speedups.
+fused time are the one-GPU analogues of the pages' block-level speedups.  Also timed:
+the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16; the same flop
+count) and the whole MLP (producer then block).
 
 The default warm-up (50 steps, about 30 ms) takes the GPU past the clock transient of
 its first launches; the timed steps then run at the sustained clock.
@@ -123,7 +125,7 @@ def main():
     import numpy as np
     import torch
     import chunked_matmul_reduce_amd as mmar
-    from workload import WORKLOADS, make_inputs
+    from workload import WORKLOADS, make_inputs, make_producer_inputs
 
     torch.cuda.set_device(0)
     if args.only == "copy":
@@ -218,6 +220,18 @@ def main():
         del Wt
         del parts
         torch.cuda.empty_cache()
+        # the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16) and the
+        # whole MLP (producer then block), on the producer's seeded inputs
+        pin = make_producer_inputs(w)
+        pd = {k: torch.from_numpy(pin[k].view(np.int16)).to("cuda").view(torch.bfloat16)
+              for k in ("X0", "W1", "b1")}
+        Hbuf = torch.empty((w.M, w.K), dtype=torch.bfloat16, device="cuda")
+        t_prod = _ev_time(torch, lambda: mmar.gelu_linear(pd["X0"], pd["W1"], pd["b1"], out=Hbuf),
+                          reps)[0]
+        t_mlp = _ev_time(torch, lambda: mmar.mlp(pd["X0"], pd["W1"], pd["b1"], W, bias, res, P, p,
+                                                 seed, out=out, hidden=Hbuf), reps)[0]
+        del pd, Hbuf
+        torch.cuda.empty_cache()
         re_bytes = (4 * P + 6) * w.M * w.N + 2 * w.N
         epi_bytes = 10 * w.M * w.N + 2 * w.N
         result["times_us"] = {k: round(v * 1e3, 2) for k, v in
@@ -231,6 +245,11 @@ def main():
         result["speedup_vs_sequential"] = round(t_seq / t_fused, 3)
         result["speedup_streams_vs_sequential"] = round(t_seq / t_str, 3)
         result["speedup_vs_unfused"] = round(t_unf / t_fused, 3)
+        result["producer_gelu"] = {"us": round(t_prod * 1e3, 2),
+                                   "TFLOP/s": round(flops / (t_prod * 1e-3) / 1e12, 2),
+                                   "shape": f"[{w.M},{w.N}] x [{w.N},{w.K}] -> bf16 [{w.M},{w.K}]"}
+        result["mlp"] = {"us": round(t_mlp * 1e3, 2),
+                         "TFLOP/s": round(2 * flops / (t_mlp * 1e-3) / 1e12, 2)}
         result["re_alone_GBps"] = round(re_bytes / (t_re * 1e-3) / 1e9, 1)
         result["epi_alone_GBps"] = round(epi_bytes / (t_epi * 1e-3) / 1e9, 1)
 

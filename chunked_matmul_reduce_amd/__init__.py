@@ -42,6 +42,7 @@ _SIGNATURES = {
     "mmar_transpose_weight": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "mmar_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_unfused": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _P]),
+    "mmar_gelu_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "mmar_gemm_only": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "mmar_gemm_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "mmar_reduce_epilogue_only": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _F, _U64, _P]),
@@ -268,6 +269,28 @@ def unfused(X, W, bias, residual, P, p_drop, seed, out=None, mask=None, stream=N
                               _stream(X.device, stream))
     _check(rc)
     return out
+
+
+def gelu_linear(X, W, bias, out=None, stream=None):
+    """mmar_gelu_linear: H = GeLU(X . W + bias) as bf16 [M, N] (the producer MatMul)."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    hp = _bits(out, "out", (M, N))
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_gelu_linear(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)),
+                                  _bits(bias, "bias", (N,)), hp, M, N, K, _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def mlp(X, W1, b1, W2, b2, residual, P, p_drop, seed, out=None, hidden=None, stream=None):
+    """The MLP around the block: H = GeLU(X . W1 + b1) (mmar_gelu_linear), then
+    out = residual + dropout(b2 + sum_p H[:, K_p] . W2[K_p, :]) (mmar_fused).  Returns
+    (out, H)."""
+    H = gelu_linear(X, W1, b1, out=hidden, stream=stream)
+    return fused(H, W2, b2, residual, P, p_drop, seed, out=out, stream=stream), H
 
 
 def gemm_only(X, W, P, chunk=(0, 0), out=None, stream=None):

@@ -66,4 +66,20 @@ __device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int
     return o;
 }
 
+// GeLU, tanh form (GPT-2's), in fp32, written as v * sigmoid(2u) = v / (1 + e^(-2u)),
+// u = sqrt(2/pi) (v + 0.044715 v^3): the same function as v/2 (1 + tanh u), without the
+// cancellation of 1 + tanh u for negative v and with one exp and one division (a few fp32
+// units of error; e^(-2u) overflowing to +inf gives -0, the limit).
+__device__ __forceinline__ float gelu_tanh_f32(float v) {
+    const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
+    return __fdividef(v, 1.0f + __expf(-2.0f * u));
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u | ((u >> 16) & 0x8000u);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 }  // namespace mmar

@@ -59,7 +59,7 @@ struct DevState {
     int id = -1;
     int cus = 0;
     std::string arch;
-    int occ[3][2] = {};  // tile kernel occupancy per mode and (bk == 64 ? 0 : 1)
+    int occ[mmar::kNumModes][2] = {};  // tile kernel occupancy per mode and (bk == 64 ? 0 : 1)
     int red_occ = 0;
     std::mutex mu;       // serializes use of the library workspace / side stream
     void* ws = nullptr;
@@ -164,7 +164,7 @@ int current_device(DevState** out) {
         st->arch = prop.gcnArchName;
         st->cus = prop.multiProcessorCount;
         if (st->arch.compare(0, 6, "gfx950") == 0) {
-            for (int m = 0; m < 3; ++m) {
+            for (int m = 0; m < mmar::kNumModes; ++m) {
                 st->occ[m][0] = mmar::tile_occupancy(m, 64);
                 st->occ[m][1] = mmar::tile_occupancy(m, 32);
             }
@@ -351,6 +351,7 @@ Plan plan_for(const DevState* st, const Shape& s, int32_t sched, int32_t cm, int
 struct Call {
     const uint16_t *X, *W, *bias, *residual;
     float* out;
+    uint16_t* hout;   // bf16 output of the producer MatMul
     Shape s;
     DropParams drop;
     bool w_t;   // W holds W^T [N, K]
@@ -386,6 +387,7 @@ TileArgs tile_args(const Call& c, int rm0, int rn0, int RM, int RN, int cm, int 
     a.bias = c.bias;
     a.residual = c.residual;
     a.out = c.out;
+    a.hout = c.hout;
     a.M = c.s.M;
     a.N = c.s.N;
     a.K = c.s.K;
@@ -744,6 +746,34 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
     c.s = s;
     const Plan p = plan_for(st, s, MMAR_SCHED_AUTO, 0, 0, 0, MMAR_W_AUTO);
     return run_plan(st, c, p, kRunPartials, nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
+                     int64_t M, int64_t N, int64_t K, void* stream) {
+    g_err.clear();
+    const Shape s{M, N, K, 1};
+    int rc;
+    if ((rc = check_shape(s))) return rc;
+    if ((rc = check_ptr(X, "X")) || (rc = check_ptr(W, "W")) || (rc = check_ptr(bias, "bias")) ||
+        (rc = check_ptr(H, "H")))
+        return rc;
+    const size_t hb = static_cast<size_t>(M * N) * 2;
+    if (overlaps(H, hb, X, static_cast<size_t>(M * K) * 2) ||
+        overlaps(H, hb, W, static_cast<size_t>(K * N) * 2) ||
+        overlaps(H, hb, bias, static_cast<size_t>(N) * 2))
+        return fail(MMAR_EINVAL, "H overlaps an input");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    Call c;
+    std::memset(&c, 0, sizeof c);
+    c.X = X;
+    c.W = W;
+    c.bias = bias;
+    c.hout = H;
+    c.s = s;
+    c.w_t = false;
+    return run_persistent(st, c, mmar::kModeGelu, static_cast<int>(M), static_cast<int>(N),
+                          static_cast<hipStream_t>(stream));
 }
 
 int mmar_unfused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,

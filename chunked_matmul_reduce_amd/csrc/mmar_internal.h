@@ -13,7 +13,9 @@ enum TileMode : int {
     kModeFused = 0,     // all P slices, reduced in registers, then bias/dropout/residual
     kModeReduced = 1,   // all P slices, reduced in registers, stored as fp32 T
     kModePartials = 2,  // one slice per work item, stored as fp32 S_p to a workspace
+    kModeGelu = 3,      // all slices (the producer MatMul has P = 1), + bias, GeLU, bf16 out
 };
+constexpr int kNumModes = 4;
 
 // Dropout parameters as the kernels use them.
 struct DropParams {
@@ -32,6 +34,7 @@ struct TileArgs {
     const uint16_t* bias;
     const uint16_t* residual;
     float* out;          // kModeFused / kModeReduced: [M, N]
+    uint16_t* hout;      // kModeGelu: bf16 [M, N]
     float* ws;           // kModePartials: [P][RM][RN] for the region
     int64_t M, N, K;
     int32_t P, Ks;       // Ks = K / P

@@ -28,8 +28,10 @@
 //     p = 0..P-1 without leaving registers.
 //   * Modes: kModeFused applies bias + Philox dropout + residual to T and stores fp32
 //     out; kModeReduced stores T; kModePartials computes one slice per work item and
-//     stores S_p to a workspace.  All three share the same MFMA sequence, so partials
-//     reduced by the reduce+epilogue kernel give the same bits as the fused mode.
+//     stores S_p to a workspace; kModeGelu (the column-parallel producer MatMul before
+//     the block) applies bias + GeLU and stores bf16.  All share the same MFMA sequence,
+//     so partials reduced by the reduce+epilogue kernel give the same bits as the fused
+//     mode.
 //   * Work items are visited chunk by chunk, tiles inside a chunk in groups of 4 tile
 //     rows; a persistent grid walks the items with a stride of the grid size, and
 //     workgroup ids are remapped so the 32 workgroups resident on one XCD (ids are
@@ -357,7 +359,38 @@ void tile_kernel(TileArgs a) {
         // arithmetic) instead of one load latency per output group.
         auto col_ok = [&](int nb) { return C::CW * wn + 32 * nb < cols; };
         auto row_ok = [&](int mb) { return C::RW * wm + 32 * mb < rows; };
-        if constexpr (MODE == kModeFused) {
+        if constexpr (MODE == kModeGelu) {
+            uint2 bb[NB][4];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int nl = min(C::CW * wn + 32 * nb, cols - 32) + 8 * g + 4 * h;
+                    bb[nb][g] = *reinterpret_cast<const uint2*>(a.bias + n0 + nl);
+                }
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        if (!col_ok(nb) || !row_ok(mb)) continue;
+                        const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
+                        const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
+                        const f32x16& acc = T[nb][mb];
+                        const uint2 b = bb[nb][g];
+                        // bf16(gelu(T + bias)), the sum and gelu in fp32
+                        auto hq = [](float t, float bv) {
+                            return bf16_rne(gelu_tanh_f32(__fadd_rn(t, bv)));
+                        };
+                        const uint32_t h0 = hq(acc[4 * g], bf16_lo(b.x));
+                        const uint32_t h1 = hq(acc[4 * g + 1], bf16_hi(b.x));
+                        const uint32_t h2 = hq(acc[4 * g + 2], bf16_lo(b.y));
+                        const uint32_t h3 = hq(acc[4 * g + 3], bf16_hi(b.y));
+                        *reinterpret_cast<uint2*>(a.hout + m * a.N + n) =
+                            make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                    }
+        } else if constexpr (MODE == kModeFused) {
             uint2 bb[NB][4], rb[NB][4][MB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -435,10 +468,12 @@ static hipError_t launch_tile_w(int mode, int bk, const TileArgs& a, int grid, h
     if (bk == 64) {
         if (mode == kModeFused) return launch_tile_t<kModeFused, 64, WT>(a, grid, s);
         if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64, WT>(a, grid, s);
+        if (mode == kModeGelu) return launch_tile_t<kModeGelu, 64, WT>(a, grid, s);
         return launch_tile_t<kModePartials, 64, WT>(a, grid, s);
     }
     if (mode == kModeFused) return launch_tile_t<kModeFused, 32, WT>(a, grid, s);
     if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32, WT>(a, grid, s);
+    if (mode == kModeGelu) return launch_tile_t<kModeGelu, 32, WT>(a, grid, s);
     return launch_tile_t<kModePartials, 32, WT>(a, grid, s);
 }
 
@@ -461,10 +496,12 @@ int tile_occupancy(int mode, int bk) {
     if (bk == 64) {
         if (mode == kModeFused) return occ_t<kModeFused, 64>();
         if (mode == kModeReduced) return occ_t<kModeReduced, 64>();
+        if (mode == kModeGelu) return occ_t<kModeGelu, 64>();
         return occ_t<kModePartials, 64>();
     }
     if (mode == kModeFused) return occ_t<kModeFused, 32>();
     if (mode == kModeReduced) return occ_t<kModeReduced, 32>();
+    if (mode == kModeGelu) return occ_t<kModeGelu, 32>();
     return occ_t<kModePartials, 32>();
 }
 

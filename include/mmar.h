@@ -155,6 +155,19 @@ int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M
 int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, int64_t M,
                        int64_t N, int64_t K, int32_t P, void* stream);
 
+/* The producer side of the block: the column-parallel MatMul that precedes it in a
+ * transformer MLP (the block sits between two MatMuls: practices record SOTA-059, "Where
+ * it stops being free"), H = GeLU(X . W + bias) with GeLU in its tanh form,
+ *   X     bf16 [M, K] row-major,  W bf16 [K, N] row-major,  bias bf16 [N],
+ *   H     bf16 [M, N] row-major (written; must not overlap an input),
+ * computed as v = fp32 sum over k (MFMA, k ascending) + bias, gelu(v) in fp32, rounded
+ * to bf16 (nearest even).  Column block p of H is what rank p of the column-parallel
+ * layer would own, and it is exactly K-slice p of the block that follows, so H feeds
+ * mmar_fused directly as its X.  Preconditions as mmar_fused with P = 1.  No
+ * workspace. */
+int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
+                     int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Comparison entry point: the same block computed unfused, one kernel per operation, the
  * way frameworks that call computation and communication as separate library kernels run
  * it (the baseline the CoCoNet record compares against, "Key takeaways", first and second

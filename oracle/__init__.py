@@ -9,7 +9,9 @@ seeded generator in ``workload``, which holds none of the block's arithmetic.
 Contents
 * ``block``  -- the block in fp64 (numpy; products and slice GEMMs through dgemm),
   the dropout mask, and an fp32 model of the declared rounding order;
-* ``philox`` -- Philox4x32-10 from Salmon et al. (SC'11), scalar and vectorized.
+* ``philox`` -- Philox4x32-10 from Salmon et al. (SC'11), scalar and vectorized;
+* ``producer`` -- the column-parallel MatMul + GeLU in front of the block, its bf16
+  rounding from fp64 and the near-tie rule for comparing a bf16 output.
 
 Pins (all in ``tests/test_oracle.py`` and ``tests/test_philox.py``): exact rational
 brute force on tiny shapes; the slice-sum invariant against the unsliced product;
@@ -17,14 +19,17 @@ p = 0 against a direct library product; p = 1 against the residual; closed-form 
 that isolate the bias, residual, scale and indexing; the kept fraction against its
 binomial spread; Philox against its constants' closed forms, against a second
 implementation, and against rocRAND's header-only Philox4x32-10 engine when a host
-compiler can build it.  Nothing on the pages prints a numeric example, so no pin comes
-from the pages themselves.
+compiler can build it; the producer's GeLU against PyTorch's tanh GeLU and the exact
+erf GeLU, its bf16 rounding against PyTorch's fp32 -> bf16 conversion and hand-made
+ties, and its product against exact rational arithmetic
+(``tests/test_producer_oracle.py``).  Nothing on the pages prints a numeric example, so
+no pin comes from the pages themselves.
 """
 from .block import (check_p, drop_threshold, keep_elements, keep_mask, keep_scale,
                     reduce_epilogue_fp32, run, run_inputs, slice_bounds, slice_partials,
                     widen)
-from . import philox
+from . import philox, producer
 
 __all__ = ["check_p", "drop_threshold", "keep_elements", "keep_mask", "keep_scale",
            "reduce_epilogue_fp32", "run", "run_inputs", "slice_bounds", "slice_partials",
-           "widen", "philox"]
+           "widen", "philox", "producer"]

@@ -1,0 +1,94 @@
+"""GPU parity of the producer MatMul (H = GeLU(X . W1 + b1), bf16) and of the MLP built
+from it and the block, through the C ABI, against the oracle.
+
+Bar for the bf16 H: every element equals the fp64 value rounded to bf16, except near a
+rounding midpoint (within the fp32 error bound), where either neighbour is accepted.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import producer
+from workload import WORKLOADS, make_producer_inputs, make_random_inputs
+from helpers import assert_within_tol, dev, host
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU-only machines, never run there
+    pytest.skip("no GPU", allow_module_level=True)
+
+import chunked_matmul_reduce_amd as mmar  # noqa: E402
+
+
+def _h_bits(H):
+    return host(H.view(torch.int16)).view(np.uint16)
+
+
+SHAPES = [(64, 256, 256), (288, 480, 160), (1056, 2048, 544), (32, 4096, 4096), (256, 96, 128)]
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_producer_against_oracle(M, K, N):
+    print("producer", M, K, N, flush=True)
+    inp = make_random_inputs(M, K, N, seed=M * 3 + N)
+    X, W, b = (dev(inp[k], torch) for k in ("X", "W", "bias"))
+    H = mmar.gelu_linear(X, W, b)
+    torch.cuda.synchronize()
+    h, _, bound = producer.producer(inp["X"], inp["W"], inp["bias"])
+    ties = producer.check_bf16_output(_h_bits(H), h, bound)
+    # the bound is generous, so many elements count as near ties; the rest must match
+    # exactly, and a wrong column, bias or GeLU would miss the bound almost everywhere
+    print("near-tie fraction", ties / (M * N), flush=True)
+    assert ties < 0.7 * M * N
+
+
+def test_producer_full_size_sampled_rows():
+    """The GPT-2 MLP block's first layer: [8192, 3072] x [3072, 12288]."""
+    w = WORKLOADS["gpt2_mlp"]
+    pin = make_producer_inputs(w)
+    X0, W1, b1 = (dev(pin[k], torch) for k in ("X0", "W1", "b1"))
+    H = mmar.gelu_linear(X0, W1, b1)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(7)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 8191], rng.choice(w.M, 90, replace=False)]))
+    h, _, bound = producer.producer(pin["X0"], pin["W1"], pin["b1"], rows=rows)
+    producer.check_bf16_output(_h_bits(H)[rows], h, bound)
+
+
+def test_mlp_tiny_against_oracle_and_bits_of_parts():
+    """mlp = gelu_linear then fused: out equals the block's oracle on the GPU's H, and
+    H equals the producer oracle (near-tie rule)."""
+    M, D, F, P = 64, 256, 512, 4                 # hidden D, MLP width F = K of the block
+    rng = np.random.default_rng(11)
+    a = make_random_inputs(M, D, F, seed=21)     # X0 [M, D], W1 [D, F], b1 [F]
+    c = make_random_inputs(M, F, D, seed=22)     # W2 [F, D], b2 [D], residual [M, D]
+    X0, W1, b1 = (dev(a[k], torch) for k in ("X", "W", "bias"))
+    W2, b2, R = (dev(c[k], torch) for k in ("W", "bias", "residual"))
+    p, seed = np.float32(0.1), int(rng.integers(1 << 40))
+    out, H = mmar.mlp(X0, W1, b1, W2, b2, R, P, p, seed)
+    torch.cuda.synchronize()
+    hb = _h_bits(H)
+    h, _, bound = producer.producer(a["X"], a["W"], a["bias"])
+    producer.check_bf16_output(hb, h, bound)
+    ora, keep = oracle.run(hb, c["W"], c["bias"], c["residual"], P, p, seed)
+    assert_within_tol(host(out), ora)
+    out2 = mmar.fused(H, W2, b2, R, P, p, seed)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(out).view(np.uint32), host(out2).view(np.uint32))
+
+
+def test_producer_rejects_bad_arguments():
+    X = torch.zeros((64, 250), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((250, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((64,), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mmar.MmarError):
+        mmar.gelu_linear(X, W, b)                 # K not a multiple of 32
+    X = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((256, 64), dtype=torch.bfloat16, device="cuda")
+    H = torch.empty((64, 64), dtype=torch.bfloat16, device="cuda")
+    assert mmar.lib.mmar_gelu_linear(X.data_ptr(), W.data_ptr(), b.data_ptr(), X.data_ptr(),
+                                     64, 64, 256, None) == mmar.EINVAL   # H overlaps X
+    mmar.gelu_linear(X, W, b, out=H)
+    torch.cuda.synchronize()
+    assert np.all(_h_bits(H) == 0)                # gelu(0) = 0

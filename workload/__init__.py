@@ -29,7 +29,7 @@ import dataclasses
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "ORDER", "f32_to_bf16_bits",
-           "make_inputs", "make_random_inputs"]
+           "make_inputs", "make_producer_inputs", "make_random_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -99,6 +99,21 @@ def make_random_inputs(M, K, N, seed, sigma_x=1.0, sigma_w=0.02, sigma_bias=0.02
     bias = _draw(rng, (N,), sigma_bias)
     res = _draw(rng, (M, N), sigma_res)
     return {"X": X, "W": W, "bias": bias, "residual": res}
+
+
+def make_producer_inputs(w: Workload | str):
+    """Inputs of the producer MatMul in front of a block (its MLP's first layer):
+    X0 [M, N] (the layer's hidden state), W1 [N, K] and b1 [K], so that
+    GeLU(X0 . W1 + b1) is the block's X [M, K].  Same recipe as ``make_inputs`` with
+    seed = the workload's seed + 100, drawn in the order X0, W1, b1 (sigma: X0 1, W1 the
+    workload's weight sigma, b1 the bias sigma)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(w.seed + 100)
+    X0 = _draw(rng, (w.M, w.N), w.sigma_x)
+    W1 = _draw(rng, (w.N, w.K), w.sigma_w)
+    b1 = _draw(rng, (w.K,), w.sigma_bias)
+    return {"X0": X0, "W1": W1, "b1": b1, "M": w.M, "N": w.K, "K": w.N}
 
 
 def make_inputs(w: Workload | str):
