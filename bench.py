@@ -15,7 +15,9 @@ legs: the sequential schedule (same kernels, no overlap), the two-stream schedul
 the unfused path (one kernel per operation, mask materialized); their ratios to the
 fused time are the one-GPU analogues of the pages' block-level speedups.  Also timed:
 the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16; the same flop
-count) and the whole MLP (producer then block).
+count), the whole MLP (producer then block), and the data-parallel side (gradient
+average of P = 8 replicas + Adam step over BERT-large's 335M parameters, HBM-bound),
+beside PyTorch's mean + fused AdamW.
 
 The default warm-up (50 steps, about 30 ms) takes the GPU past the clock transient of
 its first launches; the timed steps then run at the sustained clock.
@@ -125,7 +127,7 @@ def main():
     import numpy as np
     import torch
     import chunked_matmul_reduce_amd as mmar
-    from workload import WORKLOADS, make_inputs, make_producer_inputs
+    from workload import ADAM_WORKLOADS, WORKLOADS, make_inputs, make_producer_inputs
 
     torch.cuda.set_device(0)
     if args.only == "copy":
@@ -232,6 +234,35 @@ def main():
                                                  seed, out=out, hidden=Hbuf), reps)[0]
         del pd, Hbuf
         torch.cuda.empty_cache()
+        # the data-parallel side: gradient average + Adam step over BERT-large's parameters
+        # (seeded on the device; HBM-bound, (4P + 26) bytes per parameter)
+        aw = ADAM_WORKLOADS["bert_large_adam"]
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(aw.seed)
+        ag = torch.randn((aw.P, aw.n), generator=gen, device="cuda").mul_(1e-2)
+        ap = torch.randn(aw.n, generator=gen, device="cuda").mul_(0.02)
+        am = torch.randn(aw.n, generator=gen, device="cuda").mul_(1e-3)
+        av = torch.randn(aw.n, generator=gen, device="cuda").mul_(1e-3).square_().add_(
+            am.mul(2).square())
+        apb = torch.empty(aw.n, dtype=torch.bfloat16, device="cuda")
+        t_adam = _ev_time(torch, lambda: mmar.adam_step(ag, ap, am, av, aw.step, aw.lr, aw.beta1,
+                                                        aw.beta2, aw.eps, aw.weight_decay,
+                                                        param_bf16=apb), 20)[0]
+        t_adam_torch = None
+        try:   # PyTorch's own path for comparison: mean of the replicas, then fused AdamW
+            tp = torch.nn.Parameter(ap.clone())
+            topt = torch.optim.AdamW([tp], lr=aw.lr, betas=(aw.beta1, aw.beta2), eps=aw.eps,
+                                     weight_decay=aw.weight_decay, fused=True)
+
+            def torch_step():
+                tp.grad = ag.mean(dim=0)
+                topt.step()
+            t_adam_torch = _ev_time(torch, torch_step, 20)[0]
+            del tp, topt
+        except (RuntimeError, TypeError, ValueError):
+            t_adam_torch = None
+        del ag, ap, am, av, apb
+        torch.cuda.empty_cache()
         re_bytes = (4 * P + 6) * w.M * w.N + 2 * w.N
         epi_bytes = 10 * w.M * w.N + 2 * w.N
         result["times_us"] = {k: round(v * 1e3, 2) for k, v in
@@ -250,6 +281,11 @@ def main():
                                    "shape": f"[{w.M},{w.N}] x [{w.N},{w.K}] -> bf16 [{w.M},{w.K}]"}
         result["mlp"] = {"us": round(t_mlp * 1e3, 2),
                          "TFLOP/s": round(2 * flops / (t_mlp * 1e-3) / 1e12, 2)}
+        adam_gbs = aw.bytes / (t_adam * 1e-3) / 1e9
+        result["adam"] = {"workload": aw.desc, "us": round(t_adam * 1e3, 1),
+                          "GB/s": round(adam_gbs, 1), "frac_hbm": round(adam_gbs / PEAK_HBM_GBS, 4),
+                          "torch_mean_plus_fused_adamw_us":
+                              None if t_adam_torch is None else round(t_adam_torch * 1e3, 1)}
         result["re_alone_GBps"] = round(re_bytes / (t_re * 1e-3) / 1e9, 1)
         result["epi_alone_GBps"] = round(epi_bytes / (t_epi * 1e-3) / 1e9, 1)
 

@@ -43,6 +43,7 @@ _SIGNATURES = {
     "mmar_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_unfused": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _P]),
     "mmar_gelu_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "mmar_adam_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _F, _F, _F, _F, _F, _P]),
     "mmar_gemm_only": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "mmar_gemm_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "mmar_reduce_epilogue_only": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _F, _U64, _P]),
@@ -291,6 +292,26 @@ def mlp(X, W1, b1, W2, b2, residual, P, p_drop, seed, out=None, hidden=None, str
     (out, H)."""
     H = gelu_linear(X, W1, b1, out=hidden, stream=stream)
     return fused(H, W2, b2, residual, P, p_drop, seed, out=out, stream=stream), H
+
+
+def adam_step(grads, param, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,
+              param_bf16=None, stream=None):
+    """mmar_adam_step: average the P replicas' gradients grads [P, n] (fp32, fixed order),
+    Adam-update param, m, v (fp32 [n], in place) and, if given, write the bf16 copy of the
+    new parameters to param_bf16."""
+    torch = _torch()
+    if grads.dim() != 2:
+        raise ValueError("grads must be [P, n]")
+    P, n = (int(x) for x in grads.shape)
+    ptrs = [_f32(grads, "grads", (P, n))] + [_f32(t, nm, (n,)) for t, nm in
+                                              ((param, "param"), (m, "m"), (v, "v"))]
+    bp = None
+    if param_bf16 is not None:
+        bp = _bits(param_bf16, "param_bf16", (n,))
+    with torch.cuda.device(grads.device):
+        rc = lib.mmar_adam_step(*ptrs, bp, n, P, int(step), float(lr), float(beta1), float(beta2),
+                                float(eps), float(weight_decay), _stream(grads.device, stream))
+    _check(rc)
 
 
 def gemm_only(X, W, P, chunk=(0, 0), out=None, stream=None):

@@ -748,6 +748,62 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
     return run_plan(st, c, p, kRunPartials, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
+int mmar_adam_step(const float* grads, float* param, float* m, float* v, uint16_t* param_bf16,
+                   int64_t n, int32_t P, int64_t step, float lr, float beta1, float beta2,
+                   float eps, float weight_decay, void* stream) {
+    g_err.clear();
+    int rc;
+    if (n <= 0 || n % 4 != 0) return fail(MMAR_EINVAL, "n must be a positive multiple of 4");
+    if (P < 1 || P > 4096) return fail(MMAR_EINVAL, "P must be in [1, 4096]");
+    if (step < 1) return fail(MMAR_EINVAL, "step must be >= 1");
+    if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+        return fail(MMAR_EINVAL, "beta1 and beta2 must be in [0, 1)");
+    if (!(eps > 0.0f) || !std::isfinite(eps) || !std::isfinite(lr) ||
+        !std::isfinite(weight_decay))
+        return fail(MMAR_EINVAL, "eps must be positive; lr and weight_decay finite");
+    if ((rc = check_ptr(grads, "grads")) || (rc = check_ptr(param, "param")) ||
+        (rc = check_ptr(m, "m")) || (rc = check_ptr(v, "v")))
+        return rc;
+    if (param_bf16 && reinterpret_cast<uintptr_t>(param_bf16) % 8 != 0)
+        return fail(MMAR_EALIGN, "param_bf16 is not 8-byte aligned");
+    const size_t nb = static_cast<size_t>(n) * 4;
+    if (overlaps(param, nb, m, nb) || overlaps(param, nb, v, nb) || overlaps(m, nb, v, nb) ||
+        overlaps(grads, nb * P, param, nb) || overlaps(grads, nb * P, m, nb) ||
+        overlaps(grads, nb * P, v, nb) ||
+        (param_bf16 && (overlaps(param_bf16, nb / 2, param, nb) ||
+                        overlaps(param_bf16, nb / 2, m, nb) ||
+                        overlaps(param_bf16, nb / 2, v, nb) ||
+                        overlaps(param_bf16, nb / 2, grads, nb * P))))
+        return fail(MMAR_EINVAL, "the buffers must not overlap");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    mmar::AdamArgs a;
+    a.grads = grads;
+    a.param = param;
+    a.m = m;
+    a.v = v;
+    a.param_bf16 = param_bf16;
+    a.n = n;
+    a.P = P;
+    a.inv_p = static_cast<float>(1.0 / P);
+    a.lr = lr;
+    a.b1 = beta1;
+    a.b2 = beta2;
+    a.one_minus_b1 = static_cast<float>(1.0 - static_cast<double>(beta1));
+    a.one_minus_b2 = static_cast<float>(1.0 - static_cast<double>(beta2));
+    a.eps = eps;
+    a.wd = weight_decay;
+    a.c1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step))));
+    a.c2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
+    if (!std::isfinite(a.c1) || !std::isfinite(a.c2))
+        return fail(MMAR_EINVAL, "bias correction overflows (beta**step rounds to 1)");
+    const int64_t groups = n / 4;
+    const int grid = static_cast<int>(std::max<int64_t>(
+        1, std::min<int64_t>((groups + 255) / 256, static_cast<int64_t>(st->cus) * 8)));
+    MMAR_HIP(mmar::launch_adam(a, grid, static_cast<hipStream_t>(stream)));
+    return MMAR_OK;
+}
+
 int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
                      int64_t M, int64_t N, int64_t K, void* stream) {
     g_err.clear();

@@ -55,6 +55,18 @@ struct ReduceArgs {
     DropParams drop;
 };
 
+// Arguments of the fused reduce + Adam kernel (adam.hip).
+struct AdamArgs {
+    const float* grads;   // [P][n]
+    float* param;         // [n], updated in place
+    float* m;             // [n], first moment, updated in place
+    float* v;             // [n], second moment, updated in place
+    uint16_t* param_bf16; // [n] bf16 copy of the new parameters, or NULL
+    int64_t n;            // multiple of 4
+    int32_t P;
+    float inv_p, lr, b1, b2, one_minus_b1, one_minus_b2, eps, wd, c1, c2;
+};
+
 constexpr int kBM = 256;   // output rows per tile (4 waves x 64)
 constexpr int kBN = 128;   // output columns per tile
 constexpr int kThreads = 256;
@@ -68,6 +80,7 @@ hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t 
 // holds the whole LDS), so it runs only on CUs the tile kernel left free.
 hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, int lds_bytes, hipStream_t s);
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s);
+hipError_t launch_adam(const AdamArgs& a, int grid, hipStream_t s);
 // The unfused tail (unfused.hip): sum of the P partials ws [P][M][N] into T (may alias ws),
 // then bias add, dropout (keep bytes to mask [M][N]) and residual add into out, each its
 // own kernel on stream s.

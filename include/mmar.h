@@ -168,6 +168,23 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
 int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
                      int64_t M, int64_t N, int64_t K, void* stream);
 
+/* The data-parallel side of the CoCoNet record ("Key takeaways", fifth bullet: the
+ * gradient ReduceScatter, the optimizer and the parameter AllGather fused) folded onto
+ * one GPU, one HBM pass:
+ *   grads       fp32 [P][n]  the P data-parallel replicas' gradients (read)
+ *   param, m, v fp32 [n]     parameters, first and second Adam moments (updated in place)
+ *   param_bf16  bf16 [n]     the new parameters rounded to bf16 (written), or NULL
+ * g = (G_0 + ... + G_{P-1}) * fp32(1/P) (fixed order); m = b1 m + (1-b1) g;
+ * v = b2 v + (1-b2) g^2; p = p - lr ((m c1) / (sqrt(v c2) + eps) + weight_decay p), with
+ * c1 = 1/(1-b1^step), c2 = 1/(1-b2^step) from fp64 on the host (Adam; weight_decay > 0
+ * gives AdamW's decoupled decay).  fp32, round to nearest even, no fused multiply-add.
+ * Preconditions: n > 0 and a multiple of 4; 1 <= P <= 4096; step >= 1; 0 <= b1, b2 < 1;
+ * eps > 0; fp32 pointers 16-byte aligned, param_bf16 8-byte aligned; no buffer overlaps
+ * another.  No workspace. */
+int mmar_adam_step(const float* grads, float* param, float* m, float* v, uint16_t* param_bf16,
+                   int64_t n, int32_t P, int64_t step, float lr, float beta1, float beta2,
+                   float eps, float weight_decay, void* stream);
+
 /* Comparison entry point: the same block computed unfused, one kernel per operation, the
  * way frameworks that call computation and communication as separate library kernels run
  * it (the baseline the CoCoNet record compares against, "Key takeaways", first and second

@@ -11,7 +11,8 @@ Contents
   the dropout mask, and an fp32 model of the declared rounding order;
 * ``philox`` -- Philox4x32-10 from Salmon et al. (SC'11), scalar and vectorized;
 * ``producer`` -- the column-parallel MatMul + GeLU in front of the block, its bf16
-  rounding from fp64 and the near-tie rule for comparing a bf16 output.
+  rounding from fp64 and the near-tie rule for comparing a bf16 output;
+* ``adam`` -- the data-parallel gradient average + Adam step (fp64).
 
 Pins (all in ``tests/test_oracle.py`` and ``tests/test_philox.py``): exact rational
 brute force on tiny shapes; the slice-sum invariant against the unsliced product;
@@ -22,14 +23,15 @@ implementation, and against rocRAND's header-only Philox4x32-10 engine when a ho
 compiler can build it; the producer's GeLU against PyTorch's tanh GeLU and the exact
 erf GeLU, its bf16 rounding against PyTorch's fp32 -> bf16 conversion and hand-made
 ties, and its product against exact rational arithmetic
-(``tests/test_producer_oracle.py``).  Nothing on the pages prints a numeric example, so
+(``tests/test_producer_oracle.py``); the Adam step against PyTorch's Adam / AdamW in
+fp64 and closed forms (``tests/test_adam_oracle.py``).  Nothing on the pages prints a numeric example, so
 no pin comes from the pages themselves.
 """
 from .block import (check_p, drop_threshold, keep_elements, keep_mask, keep_scale,
                     reduce_epilogue_fp32, run, run_inputs, slice_bounds, slice_partials,
                     widen)
-from . import philox, producer
+from . import adam, philox, producer
 
 __all__ = ["check_p", "drop_threshold", "keep_elements", "keep_mask", "keep_scale",
            "reduce_epilogue_fp32", "run", "run_inputs", "slice_bounds", "slice_partials",
-           "widen", "philox", "producer"]
+           "widen", "adam", "philox", "producer"]

@@ -76,6 +76,21 @@ def test_other_entry_points_validate():
     assert "overlaps" in mmar.last_error()
     assert U(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, None, 64, 256, 256, 4, 1.5, 0, None) == \
         mmar.EINVAL   # p outside [0, 1]
+    A = L.mmar_adam_step
+    assert A(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1022, 2, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0,
+             None) == mmar.EINVAL   # n not a multiple of 4
+    assert A(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1024, 2, 0, 1e-3, 0.9, 0.999, 1e-8, 0.0,
+             None) == mmar.EINVAL   # step 0
+    assert A(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1024, 2, 1, 1e-3, 0.9, 1.0, 1e-8, 0.0,
+             None) == mmar.EINVAL   # beta2 = 1
+    assert A(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, None, 1024, 2, 1, 1e-3, 0.9, 0.999, 0.0, 0.0,
+             None) == mmar.EINVAL   # eps = 0
+    assert A(FAKE, FAKE * 2, FAKE * 2 + 1024, FAKE * 4, None, 1024, 2, 1, 1e-3, 0.9, 0.999, 1e-8,
+             0.0, None) == mmar.EINVAL   # m overlaps param
+    assert A(FAKE, FAKE * 2 + 4, FAKE * 3, FAKE * 4, None, 1024, 2, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0,
+             None) == mmar.EALIGN
+    assert L.mmar_gelu_linear(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 64, 250, None) == mmar.EINVAL
+    assert L.mmar_gelu_linear(FAKE, FAKE * 2, FAKE * 3, FAKE, 64, 64, 256, None) == mmar.EINVAL
     assert L.mmar_set_plan(64, 256, 256, 4, 9, 0, 0, 0, -1) == mmar.EINVAL
     assert L.mmar_autotune(64, 256, 250, 4, 0) == mmar.EINVAL
 

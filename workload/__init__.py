@@ -28,8 +28,8 @@ import dataclasses
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "ORDER", "f32_to_bf16_bits",
-           "make_inputs", "make_producer_inputs", "make_random_inputs"]
+__all__ = ["Workload", "WORKLOADS", "ORDER", "AdamWorkload", "ADAM_WORKLOADS", "f32_to_bf16_bits",
+           "make_adam_inputs", "make_inputs", "make_producer_inputs", "make_random_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -114,6 +114,53 @@ def make_producer_inputs(w: Workload | str):
     W1 = _draw(rng, (w.N, w.K), w.sigma_w)
     b1 = _draw(rng, (w.K,), w.sigma_bias)
     return {"X0": X0, "W1": W1, "b1": b1, "M": w.M, "N": w.K, "K": w.N}
+
+
+@dataclasses.dataclass(frozen=True)
+class AdamWorkload:
+    """A data-parallel optimizer step: n fp32 parameters, P replicas' gradients."""
+    name: str
+    n: int
+    P: int
+    seed: int
+    step: int = 10
+    lr: float = 1e-4
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+    desc: str = ""
+
+    @property
+    def bytes(self) -> int:
+        """HBM bytes of one fused step: P gradient reads, parameter and both moments read
+        and written, the bf16 parameter copy written."""
+        return (4 * self.P + 26) * self.n
+
+
+ADAM_WORKLOADS = {
+    # BERT-large (about 335M parameters) with 8 data-parallel replicas
+    "bert_large_adam": AdamWorkload("bert_large_adam", 335_141_888, 8, 5,
+                                    desc="BERT-large, 335M fp32 parameters, P=8 replicas"),
+    # a smaller case the oracle checks element by element
+    "adam_16m": AdamWorkload("adam_16m", 16 * 1024 * 1024, 8, 6,
+                             desc="16M fp32 parameters, P=8 replicas"),
+}
+
+
+def make_adam_inputs(n: int, P: int, seed: int):
+    """Seeded fp32 optimizer state and gradients: PCG64 ``default_rng(seed)``, drawn in the
+    order grads [P, n] (sigma 1e-2), param [n] (0.02), m [n] (1e-3), d [n] (1e-3), all
+    float32, with v = (2 m)^2 + d^2: a second moment consistent with the first, as along
+    an Adam run (|m| / sqrt(v) <= 1/2)."""
+    rng = np.random.default_rng(seed)
+    f = np.float32
+    grads = rng.standard_normal((P, n), dtype=np.float32) * f(1e-2)
+    param = rng.standard_normal(n, dtype=np.float32) * f(0.02)
+    m = rng.standard_normal(n, dtype=np.float32) * f(1e-3)
+    d = rng.standard_normal(n, dtype=np.float32) * f(1e-3)
+    v = np.square(f(2) * m) + np.square(d)
+    return {"grads": grads, "param": param, "m": m, "v": v}
 
 
 def make_inputs(w: Workload | str):
