@@ -40,11 +40,14 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "fused GEMM+reduce+epilogue TFLOP/s, % bf16 MFMA peak, % epilogue hidden"
 
 
-def _ev_time(torch, fn, reps):
-    """Median and mean of per-call durations (ms), HIP events on the current stream."""
+def _ev_time(torch, fn, reps, before=None, stats=False):
+    """Median and mean of per-call durations (ms), HIP events on the current stream.
+    ``before`` runs (untimed) ahead of every call; ``stats`` adds min and p90."""
     s = torch.cuda.current_stream()
     times = []
     for _ in range(reps):
+        if before is not None:
+            before()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(s)
@@ -53,7 +56,10 @@ def _ev_time(torch, fn, reps):
         e1.synchronize()
         times.append(e0.elapsed_time(e1))
     times.sort()
-    return times[len(times) // 2], sum(times) / len(times)
+    med, mean = times[len(times) // 2], sum(times) / len(times)
+    if stats:
+        return med, mean, times[0], times[min(len(times) - 1, int(0.9 * (len(times) - 1) + 0.5))]
+    return med, mean
 
 
 TILE_KERNEL_SOURCES = ("tile_kernel.hip", "device_common.h", "mmar_internal.h")
@@ -196,7 +202,12 @@ def main():
 
     if args.only == "all":
         reps = max(10, args.steps)
-        t_fused = _ev_time(torch, fused, reps)[0]
+        t_fused, _, t_fused_min, t_fused_p90 = _ev_time(torch, fused, reps, stats=True)
+        # cold caches: write 1 GiB (more than the 8 x 4 MB L2 and the 256 MB MALL) before
+        # every call
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        t_cold = _ev_time(torch, fused, max(10, reps // 4), before=lambda: flush.fill_(1.0))[0]
+        del flush
         T = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
         t_gemm = _ev_time(torch, lambda: mmar.gemm_only(X, W, P, out=T), reps)[0]
         parts = torch.empty((P, w.M, w.N), dtype=torch.float32, device="cuda")
@@ -271,6 +282,9 @@ def main():
                                "streams": t_str, "unfused": t_unf, "persistent_w_direct": t_dir,
                                "persistent_w_pretranspose": t_pre, "w_transpose": t_tr,
                                "persistent_w_given_transposed": t_nt}.items()}
+        result["fused_us_stats"] = {"median": round(t_fused * 1e3, 2), "min": round(t_fused_min * 1e3, 2),
+                                    "p90": round(t_fused_p90 * 1e3, 2),
+                                    "median_cold_caches": round(t_cold * 1e3, 2)}
         result["hidden_fraction"] = round(1.0 - (t_fused - t_gemm) / t_re, 4)
         result["hidden_fraction_epilogue"] = round(1.0 - (t_fused - t_gemm) / t_epi, 4)
         result["speedup_vs_sequential"] = round(t_seq / t_fused, 3)
