@@ -9,6 +9,9 @@ Block computed (see include/mmar.h for the full contract):
     out = residual + dropout_p(bias + sum_p X[:, K_p] @ W[K_p, :])     (fp32 out)
 with bf16 X [M,K], W [K,N], bias [N], residual [M,N]; P equal K-slices; fp32 slice
 accumulation from zero; fixed-order fp32 reduction; counter-based Philox4x32-10 mask.
+Around it: ``gelu_linear`` / ``mlp`` (the producer MatMul + GeLU in front of the block),
+``unfused`` (the block one kernel per operation) and ``adam_step`` (the data-parallel
+gradient average + Adam step).
 """
 from __future__ import annotations
 

@@ -270,6 +270,22 @@ size_t ws_bytes_for(const Shape& s, const Plan& p, bool w_given_t) {
     return wt_bytes_for(s, p, w_given_t) + ring_bytes_for(s, p);
 }
 
+// A plan read from the cache file is used only if it is one set_plan would accept for
+// its shape (the file may be stale or edited by hand).
+bool plan_is_valid(const Shape& s, const Plan& p) {
+    const bool shape_ok = s.M > 0 && s.N > 0 && s.K > 0 && s.P >= 1 && s.P <= 4096 &&
+                          s.K % s.P == 0 && (s.K / s.P) % 32 == 0 && s.M % 32 == 0 &&
+                          s.N % 32 == 0;
+    const bool chunk_ok = p.cm > 0 && p.cn > 0 && p.cm % 32 == 0 && p.cn % 32 == 0 &&
+                          s.M % p.cm == 0 && s.N % p.cn == 0;
+    const bool sched_ok = p.sched == MMAR_SCHED_SEQUENTIAL || p.sched == MMAR_SCHED_STREAMS ||
+                          p.sched == MMAR_SCHED_PERSISTENT;
+    const bool ring_ok = p.ring >= 0 && p.ring <= kMaxRing &&
+                         (p.sched != MMAR_SCHED_STREAMS || p.ring >= 1);
+    const bool w_ok = p.wmode == MMAR_W_DIRECT || p.wmode == MMAR_W_PRETRANSPOSE;
+    return shape_ok && chunk_ok && sched_ok && ring_ok && w_ok;
+}
+
 void load_plan_cache_locked() {
     if (g_plans_loaded) return;
     g_plans_loaded = true;
@@ -293,7 +309,7 @@ void load_plan_cache_locked() {
             p.cn = cn;
             p.ring = ring;
             p.wmode = wmode;
-            g_plans[PlanKey(arch, M, N, K, P)] = p;
+            if (plan_is_valid(Shape{M, N, K, P}, p)) g_plans[PlanKey(arch, M, N, K, P)] = p;
         }
     }
     std::fclose(f);

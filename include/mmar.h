@@ -54,8 +54,9 @@
  * Ownership.  The caller owns every tensor and keeps it alive until the stream has
  * passed the call; the library never frees or retains caller memory.  The library owns
  * a per-device workspace (partial-product ring, pre-transposed weight), a second stream
- * and events, created on first use and freed by mmar_release().  Calls that use the library workspace are serialized per device by a
- * mutex; with a caller workspace (mmar_fused_ex) calls are re-entrant.
+ * and events, created on first use and freed by mmar_release().  Calls that use the
+ * library workspace are serialized per device by a mutex; with a caller workspace
+ * (mmar_fused_ex) calls are re-entrant.
  *
  * Errors.  Every int-returning call returns MMAR_OK (0) or a negative code; details of
  * the last failure on the calling thread are in mmar_last_error().  Asynchronous device
@@ -66,6 +67,10 @@
  * work is ordered after earlier work on `stream` and before later work on it: the
  * second stream of MMAR_SCHED_STREAMS waits for `stream` on entry and `stream` waits
  * for it before the call returns.
+ *
+ * Around the block: mmar_gelu_linear (the column-parallel MatMul + GeLU that produces the
+ * block's X), mmar_unfused (the block one kernel per operation, for comparison) and
+ * mmar_adam_step (the data-parallel gradient average + Adam step, one HBM pass).
  */
 #ifndef MMAR_H
 #define MMAR_H
