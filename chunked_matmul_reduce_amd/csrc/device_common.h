@@ -66,13 +66,25 @@ __device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int
     return o;
 }
 
-// GeLU, tanh form (GPT-2's), in fp32, written as v * sigmoid(2u) = v / (1 + e^(-2u)),
-// u = sqrt(2/pi) (v + 0.044715 v^3): the same function as v/2 (1 + tanh u), without the
-// cancellation of 1 + tanh u for negative v and with one exp and one division (a few fp32
-// units of error; e^(-2u) overflowing to +inf gives -0, the limit).
+// GeLU, tanh form (GPT-2's), in fp32, written as v * sigmoid(2u) = v / (1 + 2^w) with
+// u = sqrt(2/pi) (v + 0.044715 v^3) and w = -2 u log2(e) = v (K1 + K2 v^2): the same
+// function as v/2 (1 + tanh u), without the cancellation of 1 + tanh u for negative v;
+// one v_exp_f32 and one v_rcp_f32 (about 1 fp32 unit each) and an explicit FMA.  2^w
+// overflowing to +inf gives -0, the limit.
 __device__ __forceinline__ float gelu_tanh_f32(float v) {
-    const float u = 0.7978845608028654f * (v + 0.044715f * v * v * v);
-    return __fdividef(v, 1.0f + __expf(-2.0f * u));
+    constexpr float K1 = -2.0f * 0.7978845608028654f * 1.4426950408889634f;
+    constexpr float K2 = K1 * 0.044715f;
+    const float w = v * __builtin_fmaf(K2, v * v, K1);
+    return v * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(w));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (round to nearest even; v_cvt_pk_bf16_f32), first in the low half.
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // fp32 -> bf16 bits, round to nearest even (NaN -> quiet NaN).

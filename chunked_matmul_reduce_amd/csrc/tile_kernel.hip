@@ -380,15 +380,15 @@ void tile_kernel(TileArgs a) {
                         const f32x16& acc = T[nb][mb];
                         const uint2 b = bb[nb][g];
                         // bf16(gelu(T + bias)), the sum and gelu in fp32
-                        auto hq = [](float t, float bv) {
-                            return bf16_rne(gelu_tanh_f32(__fadd_rn(t, bv)));
+                        auto gq = [](float t, float bv) {
+                            return gelu_tanh_f32(__fadd_rn(t, bv));
                         };
-                        const uint32_t h0 = hq(acc[4 * g], bf16_lo(b.x));
-                        const uint32_t h1 = hq(acc[4 * g + 1], bf16_hi(b.x));
-                        const uint32_t h2 = hq(acc[4 * g + 2], bf16_lo(b.y));
-                        const uint32_t h3 = hq(acc[4 * g + 3], bf16_hi(b.y));
+                        const float g0 = gq(acc[4 * g], bf16_lo(b.x));
+                        const float g1 = gq(acc[4 * g + 1], bf16_hi(b.x));
+                        const float g2 = gq(acc[4 * g + 2], bf16_lo(b.y));
+                        const float g3 = gq(acc[4 * g + 3], bf16_hi(b.y));
                         *reinterpret_cast<uint2*>(a.hout + m * a.N + n) =
-                            make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                            make_uint2(bf16x2_rne(g0, g1), bf16x2_rne(g2, g3));
                     }
         } else if constexpr (MODE == kModeFused) {
             uint2 bb[NB][4], rb[NB][4][MB];
