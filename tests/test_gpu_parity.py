@@ -89,6 +89,7 @@ RAGGED = [
     (64, 64, 32, 1),
     (1056, 2048, 544, 8),
     (32, 4096, 4096, 2),
+    (64, 131072, 64, 4096),   # the largest P: 4096 slices of K/P = 32
 ]
 
 
@@ -342,3 +343,35 @@ def test_unfused_matches_fused_bits_and_oracle_mask(case):
         f = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, pp, seed)
         torch.cuda.synchronize()
         assert np.array_equal(f32_bits(host(u)), f32_bits(host(f))), pp
+
+
+# ---------------------------------------------------------------- maximum sizes
+def test_largest_tensor_offsets():
+    """X at the 2^31-element limit (M = 256, K = 8 355 840, 4.3 GB): the per-tile byte
+    offsets of the far end of X approach 2^32.  Structured integer inputs make every
+    schedule's fp32 result exact: X row m holds 2 at column (13 m) mod 1000 and 1 at
+    column K - 1 - 7 (m mod 64), zeros elsewhere; W, bias, residual hold small integers;
+    p = 0.  Expected: out[m] = 2 W[(13 m) mod 1000] + W[K - 1 - 7 (m mod 64)] + bias +
+    residual, exactly."""
+    M, P, Ks, N = 256, 1024, 8160, 32
+    K = P * Ks
+    assert M * K < 2 ** 31
+    g = torch.Generator(device="cuda")
+    g.manual_seed(31)
+    X = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    rows = torch.arange(M, device="cuda")
+    c_lo = (13 * rows) % 1000
+    c_hi = K - 1 - 7 * (rows % 64)
+    X[rows, c_lo] = 2.0
+    X[rows, c_hi] = 1.0
+    W = torch.randint(-8, 9, (K, N), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    b = torch.randint(-4, 5, (N,), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    R = torch.randint(-4, 5, (M, N), generator=g, device="cuda", dtype=torch.int8).to(torch.bfloat16)
+    out = mmar.fused(X, W, b, R, P, 0.0, 7)
+    torch.cuda.synchronize()
+    w_lo = host(W[c_lo].float()).astype(np.float64)
+    w_hi = host(W[c_hi].float()).astype(np.float64)
+    want = 2 * w_lo + w_hi + host(b.float())[None, :] + host(R.float())
+    assert np.array_equal(host(out).astype(np.float64), want)
+    del X, W
+    torch.cuda.empty_cache()
