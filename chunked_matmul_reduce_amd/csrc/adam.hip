@@ -26,32 +26,49 @@ __device__ __forceinline__ void adam1(float g, float& p, float& m, float& v, con
     p = __fsub_rn(p, __fmul_rn(a.lr, upd));
 }
 
-// One thread per group of four parameters (n is a multiple of 4).
+// Every byte is touched once, so all loads and stores are nontemporal (streamed past the
+// caches instead of evicting other data into them).
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4_t ld_stream(const float* base, int64_t q) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(base) + q);
+}
+__device__ __forceinline__ void st_stream(float* base, int64_t q, f32x4_t v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(base) + q);
+}
+
+// One thread per group of four parameters (n is a multiple of 4); launched with one
+// thread per group, the loop only runs again when the grid is capped.
 __global__ __launch_bounds__(256) void adam_kernel(AdamArgs a) {
     const int64_t groups = a.n / 4;
     const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
     for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < groups; q += stride) {
-        float4 g = reinterpret_cast<const float4*>(a.grads)[q];
+        f32x4_t g = ld_stream(a.grads, q);
         for (int r = 1; r < a.P; ++r) {
-            const float4 s = reinterpret_cast<const float4*>(a.grads + r * a.n)[q];
+            const f32x4_t s = ld_stream(a.grads + r * a.n, q);
             g.x = __fadd_rn(g.x, s.x);
             g.y = __fadd_rn(g.y, s.y);
             g.z = __fadd_rn(g.z, s.z);
             g.w = __fadd_rn(g.w, s.w);
         }
-        float4 p = reinterpret_cast<float4*>(a.param)[q];
-        float4 m = reinterpret_cast<float4*>(a.m)[q];
-        float4 v = reinterpret_cast<float4*>(a.v)[q];
-        adam1(__fmul_rn(g.x, a.inv_p), p.x, m.x, v.x, a);
-        adam1(__fmul_rn(g.y, a.inv_p), p.y, m.y, v.y, a);
-        adam1(__fmul_rn(g.z, a.inv_p), p.z, m.z, v.z, a);
-        adam1(__fmul_rn(g.w, a.inv_p), p.w, m.w, v.w, a);
-        reinterpret_cast<float4*>(a.param)[q] = p;
-        reinterpret_cast<float4*>(a.m)[q] = m;
-        reinterpret_cast<float4*>(a.v)[q] = v;
-        if (a.param_bf16)
-            reinterpret_cast<uint2*>(a.param_bf16)[q] = make_uint2(
-                bf16_rne(p.x) | (bf16_rne(p.y) << 16), bf16_rne(p.z) | (bf16_rne(p.w) << 16));
+        const f32x4_t p4 = ld_stream(a.param, q), m4 = ld_stream(a.m, q), v4 = ld_stream(a.v, q);
+        float p[4], m[4], v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            p[i] = p4[i];
+            m[i] = m4[i];
+            v[i] = v4[i];
+            adam1(__fmul_rn(g[i], a.inv_p), p[i], m[i], v[i], a);
+        }
+        st_stream(a.param, q, f32x4_t{p[0], p[1], p[2], p[3]});
+        st_stream(a.m, q, f32x4_t{m[0], m[1], m[2], m[3]});
+        st_stream(a.v, q, f32x4_t{v[0], v[1], v[2], v[3]});
+        if (a.param_bf16) {
+            const u32x2_t h = {bf16_rne(p[0]) | (bf16_rne(p[1]) << 16),
+                               bf16_rne(p[2]) | (bf16_rne(p[3]) << 16)};
+            __builtin_nontemporal_store(h, reinterpret_cast<u32x2_t*>(a.param_bf16) + q);
+        }
     }
 }
 

@@ -813,9 +813,11 @@ int mmar_adam_step(const float* grads, float* param, float* m, float* v, uint16_
     a.c2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
     if (!std::isfinite(a.c1) || !std::isfinite(a.c2))
         return fail(MMAR_EINVAL, "bias correction overflows (beta**step rounds to 1)");
+    // one thread per group of four parameters (a full grid streams faster than a
+    // grid-stride loop over a few blocks per CU); capped at the grid-size limit
     const int64_t groups = n / 4;
-    const int grid = static_cast<int>(std::max<int64_t>(
-        1, std::min<int64_t>((groups + 255) / 256, static_cast<int64_t>(st->cus) * 8)));
+    const int grid = static_cast<int>(std::min<int64_t>((groups + 255) / 256, INT32_MAX));
+    (void)st;
     MMAR_HIP(mmar::launch_adam(a, grid, static_cast<hipStream_t>(stream)));
     return MMAR_OK;
 }
