@@ -9,6 +9,10 @@ shard is exactly the K-slice p the row-parallel block consumes, so no collective
 between the two; folded onto one device it is one MatMul with a bias + GeLU tail whose
 bf16 output H is the block's X.
 
+For the attention block the MatMul in front is the QKV projection: the same column-
+parallel MatMul + bias with no activation (H = X . W + b), so ``producer`` takes the
+activation as an argument ("gelu_tanh" or "none").
+
 Readings (the pages name the MLP but give no formula):
 
 * GeLU is the tanh form used by GPT-2: gelu(v) = v/2 * (1 + tanh(sqrt(2/pi) * (v +
@@ -72,10 +76,15 @@ def bf16_ulp(x):
     return np.ldexp(1.0, np.maximum(e, -125) - 8)
 
 
-def producer(X, W1, b1, rows=None):
-    """H = GeLU(X . W1 + b1).  Returns (h fp64, H bf16 bits, bound fp64) for the listed
-    rows (all by default); ``bound`` is the per-element error bound of an fp32
-    computation of h (see ``near_tie``)."""
+ACTIVATIONS = ("gelu_tanh", "none")
+
+
+def producer(X, W1, b1, rows=None, activation="gelu_tanh"):
+    """H = act(X . W1 + b1), act = GeLU (tanh form) or the identity ("none").  Returns
+    (h fp64, H bf16 bits, bound fp64) for the listed rows (all by default); ``bound`` is
+    the per-element error bound of an fp32 computation of h (see ``near_tie``)."""
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {ACTIVATIONS}")
     X = np.asarray(X)
     W1 = np.asarray(W1)
     b1 = np.asarray(b1)
@@ -86,8 +95,12 @@ def producer(X, W1, b1, rows=None):
     # magnitudes (generous: 64 units), carried through gelu (|gelu'| < 1.13), plus a few
     # fp32 units of gelu itself
     mag = np.abs(x64) @ np.abs(w64) + np.abs(widen(b1))[None, :]
-    h = gelu_tanh(v)
-    bound = 1.13 * 64.0 * 2.0 ** -24 * mag + 2.0 ** -20 * np.abs(h)
+    if activation == "gelu_tanh":
+        h = gelu_tanh(v)
+        bound = 1.13 * 64.0 * 2.0 ** -24 * mag + 2.0 ** -20 * np.abs(h)
+    else:
+        h = v
+        bound = 64.0 * 2.0 ** -24 * mag + 2.0 ** -22 * np.abs(h)
     _, bits = round_bf16(h)
     return h, bits, bound
 

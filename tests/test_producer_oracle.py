@@ -115,3 +115,48 @@ def test_check_bf16_output_near_zero_after_cancellation():
     g[0] = exact[0] + 200                            # ~6e-6 away: beyond the bound
     with pytest.raises(AssertionError):
         producer.check_bf16_output(g, h, bound)
+
+
+def test_linear_without_activation_is_exact_on_tiny_shapes():
+    """activation="none" (the QKV projection): v = X . W1 + b1 against exact rational
+    arithmetic, rounded once to bf16."""
+    inp = make_random_inputs(5, 12, 7, seed=8)
+    X, W, b = inp["X"], inp["W"], inp["bias"]
+    h, bits, bound = producer.producer(X, W, b, activation="none")
+    x, w, bb = widen(X), widen(W), widen(b)
+    for i in range(5):
+        for j in range(7):
+            exact = sum(Fraction(float(x[i, k])) * Fraction(float(w[k, j])) for k in range(12)) + \
+                Fraction(float(bb[j]))
+            assert abs(Fraction(h[i, j]) - exact) <= Fraction(2.0 ** -50) * max(1, abs(exact))
+    _, expect = producer.round_bf16(h)
+    assert np.array_equal(bits, expect)
+    # the GeLU variant of the same inputs differs (the activation is really applied there)
+    hg, _, _ = producer.producer(X, W, b)
+    assert not np.allclose(hg, h)
+    with pytest.raises(ValueError):
+        producer.producer(X, W, b, activation="relu")
+
+
+def test_linear_one_hot_rows_and_double_rounding_pin():
+    """One-hot X rows copy W1 rows plus b1 exactly; a row whose sum lies just above a bf16
+    midpoint rounds up (the direct fp64 rounding), and the GPU's fp32 sum, which lands on
+    the midpoint and rounds to even, is accepted only as a near tie."""
+    rng = np.random.default_rng(9)
+    W1 = f32_to_bf16_bits(rng.standard_normal((4, 6)).astype(np.float32))
+    b1 = f32_to_bf16_bits(rng.standard_normal(6).astype(np.float32))
+    X = np.zeros((4, 4), np.uint16)
+    X[np.arange(4), np.arange(4)] = 0x3F80
+    h, _, _ = producer.producer(X, W1, b1, activation="none")
+    np.testing.assert_array_equal(h, widen(W1) + widen(b1)[None, :])
+    # 1 + 2^-8 + 2^-40: X row (1, 2^-8, 2^-40) against a column of ones, bias 0
+    Xd = f32_to_bf16_bits(np.array([[1.0, 2.0 ** -8, 2.0 ** -40]], np.float32))
+    Wd = f32_to_bf16_bits(np.ones((3, 1), np.float32))
+    bd = np.zeros(1, np.uint16)
+    h, bits, bound = producer.producer(Xd, Wd, bd, activation="none")
+    assert h[0, 0] == 1.0 + 2.0 ** -8 + 2.0 ** -40
+    assert bits[0, 0] == 0x3F81
+    assert producer.near_tie(h, bound)[0, 0]
+    assert producer.check_bf16_output(np.array([[0x3F80]], np.uint16), h, bound) == 1
+    with pytest.raises(AssertionError):
+        producer.check_bf16_output(np.array([[0x3F82]], np.uint16), h, bound)
