@@ -15,7 +15,8 @@ legs: the sequential schedule (same kernels, no overlap), the two-stream schedul
 the unfused path (one kernel per operation, mask materialized); their ratios to the
 fused time are the one-GPU analogues of the pages' block-level speedups.  Also timed:
 the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16; the same flop
-count), the whole MLP (producer then block), and the data-parallel side (gradient
+count), the whole MLP (producer then block), the QKV projection in front of the GPT-2
+attention block (bias, no activation), and the data-parallel side (gradient
 average of P = 8 replicas + Adam step over BERT-large's 335M parameters, HBM-bound),
 beside PyTorch's mean + fused AdamW.
 
@@ -133,7 +134,8 @@ def main():
     import numpy as np
     import torch
     import chunked_matmul_reduce_amd as mmar
-    from workload import ADAM_WORKLOADS, WORKLOADS, make_inputs, make_producer_inputs
+    from workload import (ADAM_WORKLOADS, WORKLOADS, make_inputs, make_producer_inputs,
+                          make_qkv_inputs)
 
     torch.cuda.set_device(0)
     if args.only == "copy":
@@ -245,6 +247,18 @@ def main():
                                                  seed, out=out, hidden=Hbuf), reps)[0]
         del pd, Hbuf
         torch.cuda.empty_cache()
+        # the QKV projection in front of the GPT-2 attention block (bias, no activation):
+        # [8192, 3072] x [3072, 9216], whichever block workload is timed
+        qw = WORKLOADS["gpt2_attn"]
+        qin = make_qkv_inputs(qw)
+        qd = {k: torch.from_numpy(qin[k].view(np.int16)).to("cuda").view(torch.bfloat16)
+              for k in ("X0", "Wqkv", "bqkv")}
+        Qbuf = torch.empty((qw.M, 3 * qw.K), dtype=torch.bfloat16, device="cuda")
+        t_qkv = _ev_time(torch, lambda: mmar.linear(qd["X0"], qd["Wqkv"], qd["bqkv"], "none",
+                                                    out=Qbuf), reps)[0]
+        qkv_flops = 2 * qw.M * qw.N * 3 * qw.K
+        del qd, Qbuf
+        torch.cuda.empty_cache()
         # the data-parallel side: gradient average + Adam step over BERT-large's parameters
         # (seeded on the device; HBM-bound, (4P + 26) bytes per parameter)
         aw = ADAM_WORKLOADS["bert_large_adam"]
@@ -295,6 +309,10 @@ def main():
                                    "shape": f"[{w.M},{w.N}] x [{w.N},{w.K}] -> bf16 [{w.M},{w.K}]"}
         result["mlp"] = {"us": round(t_mlp * 1e3, 2),
                          "TFLOP/s": round(2 * flops / (t_mlp * 1e-3) / 1e12, 2)}
+        result["producer_qkv"] = {"us": round(t_qkv * 1e3, 2),
+                                  "TFLOP/s": round(qkv_flops / (t_qkv * 1e-3) / 1e12, 2),
+                                  "shape": f"[{qw.M},{qw.N}] x [{qw.N},{3 * qw.K}] -> bf16 "
+                                           f"[{qw.M},{3 * qw.K}], bias, no activation"}
         adam_gbs = aw.bytes / (t_adam * 1e-3) / 1e9
         result["adam"] = {"workload": aw.desc, "us": round(t_adam * 1e3, 1),
                           "GB/s": round(adam_gbs, 1), "frac_hbm": round(adam_gbs / PEAK_HBM_GBS, 4),

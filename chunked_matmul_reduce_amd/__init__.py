@@ -9,7 +9,8 @@ Block computed (see include/mmar.h for the full contract):
     out = residual + dropout_p(bias + sum_p X[:, K_p] @ W[K_p, :])     (fp32 out)
 with bf16 X [M,K], W [K,N], bias [N], residual [M,N]; P equal K-slices; fp32 slice
 accumulation from zero; fixed-order fp32 reduction; counter-based Philox4x32-10 mask.
-Around it: ``gelu_linear`` / ``mlp`` (the producer MatMul + GeLU in front of the block),
+Around it: ``linear`` / ``gelu_linear`` / ``mlp`` (the producer MatMul + bias and GeLU,
+or no activation for an attention block's QKV projection, in front of the block),
 ``unfused`` (the block one kernel per operation) and ``adam_step`` (the data-parallel
 gradient average + Adam step).
 """
@@ -46,6 +47,7 @@ _SIGNATURES = {
     "mmar_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_unfused": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _P]),
     "mmar_gelu_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "mmar_linear": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "mmar_adam_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I32, _I64, _F, _F, _F, _F, _F, _P]),
     "mmar_gemm_only": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _I32, _I32, _P]),
     "mmar_gemm_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _P]),
@@ -285,6 +287,26 @@ def gelu_linear(X, W, bias, out=None, stream=None):
     with torch.cuda.device(X.device):
         rc = lib.mmar_gelu_linear(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)),
                                   _bits(bias, "bias", (N,)), hp, M, N, K, _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+ACTIVATIONS = {"none": 0, "gelu_tanh": 1}   # MMAR_ACT_NONE, MMAR_ACT_GELU_TANH
+
+
+def linear(X, W, bias, activation="none", out=None, stream=None):
+    """mmar_linear: H = act(X . W + bias) as bf16 [M, N], act "none" (the QKV projection in
+    front of an attention block) or "gelu_tanh" (as gelu_linear)."""
+    torch = _torch()
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}")
+    M, N, K = _shapes(X, W, 1)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    hp = _bits(out, "out", (M, N))
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_linear(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), _bits(bias, "bias", (N,)),
+                             hp, M, N, K, ACTIVATIONS[activation], _stream(X.device, stream))
     _check(rc)
     return out
 

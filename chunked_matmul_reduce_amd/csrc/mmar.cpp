@@ -368,6 +368,7 @@ struct Call {
     const uint16_t *X, *W, *bias, *residual;
     float* out;
     uint16_t* hout;   // bf16 output of the producer MatMul
+    int act;          // its activation (mmar::Activation)
     Shape s;
     DropParams drop;
     bool w_t;   // W holds W^T [N, K]
@@ -404,6 +405,7 @@ TileArgs tile_args(const Call& c, int rm0, int rn0, int RM, int RN, int cm, int 
     a.residual = c.residual;
     a.out = c.out;
     a.hout = c.hout;
+    a.act = c.act;
     a.M = c.s.M;
     a.N = c.s.N;
     a.K = c.s.K;
@@ -822,9 +824,11 @@ int mmar_adam_step(const float* grads, float* param, float* m, float* v, uint16_
     return MMAR_OK;
 }
 
-int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
-                     int64_t M, int64_t N, int64_t K, void* stream) {
+int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
+                int64_t M, int64_t N, int64_t K, int32_t activation, void* stream) {
     g_err.clear();
+    if (activation != MMAR_ACT_NONE && activation != MMAR_ACT_GELU_TANH)
+        return fail(MMAR_EINVAL, "activation must be MMAR_ACT_NONE or MMAR_ACT_GELU_TANH");
     const Shape s{M, N, K, 1};
     int rc;
     if ((rc = check_shape(s))) return rc;
@@ -844,10 +848,16 @@ int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
     c.W = W;
     c.bias = bias;
     c.hout = H;
+    c.act = activation == MMAR_ACT_GELU_TANH ? mmar::kActGeluTanh : mmar::kActNone;
     c.s = s;
     c.w_t = false;
-    return run_persistent(st, c, mmar::kModeGelu, static_cast<int>(M), static_cast<int>(N),
+    return run_persistent(st, c, mmar::kModeLinear, static_cast<int>(M), static_cast<int>(N),
                           static_cast<hipStream_t>(stream));
+}
+
+int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
+                     int64_t M, int64_t N, int64_t K, void* stream) {
+    return mmar_linear(X, W, bias, H, M, N, K, MMAR_ACT_GELU_TANH, stream);
 }
 
 int mmar_unfused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,

@@ -13,9 +13,16 @@ enum TileMode : int {
     kModeFused = 0,     // all P slices, reduced in registers, then bias/dropout/residual
     kModeReduced = 1,   // all P slices, reduced in registers, stored as fp32 T
     kModePartials = 2,  // one slice per work item, stored as fp32 S_p to a workspace
-    kModeGelu = 3,      // all slices (the producer MatMul has P = 1), + bias, GeLU, bf16 out
+    kModeLinear = 3,    // all slices (the producer MatMul has P = 1), + bias, activation,
+                        // bf16 out
 };
 constexpr int kNumModes = 4;
+
+// Activation of kModeLinear (the values of the public MMAR_ACT_* constants).
+enum Activation : int {
+    kActNone = 0,       // H = X . W + bias (the attention block's QKV projection)
+    kActGeluTanh = 1,   // H = GeLU(X . W + bias), tanh form (the MLP's first MatMul)
+};
 
 // Dropout parameters as the kernels use them.
 struct DropParams {
@@ -34,13 +41,14 @@ struct TileArgs {
     const uint16_t* bias;
     const uint16_t* residual;
     float* out;          // kModeFused / kModeReduced: [M, N]
-    uint16_t* hout;      // kModeGelu: bf16 [M, N]
+    uint16_t* hout;      // kModeLinear: bf16 [M, N]
     float* ws;           // kModePartials: [P][RM][RN] for the region
     int64_t M, N, K;
     int32_t P, Ks;       // Ks = K / P
     int32_t rm0, rn0, RM, RN;
     int32_t cm, cn;
     int32_t total_items; // tiles (x P for kModePartials)
+    int32_t act;         // kModeLinear: Activation
     DropParams drop;
 };
 

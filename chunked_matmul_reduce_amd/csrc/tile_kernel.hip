@@ -28,8 +28,9 @@
 //     p = 0..P-1 without leaving registers.
 //   * Modes: kModeFused applies bias + Philox dropout + residual to T and stores fp32
 //     out; kModeReduced stores T; kModePartials computes one slice per work item and
-//     stores S_p to a workspace; kModeGelu (the column-parallel producer MatMul before
-//     the block) applies bias + GeLU and stores bf16.  All share the same MFMA sequence,
+//     stores S_p to a workspace; kModeLinear (the column-parallel producer MatMul before
+//     the block) applies bias and GeLU or no activation and stores bf16.  All share the
+//     same MFMA sequence,
 //     so partials reduced by the reduce+epilogue kernel give the same bits as the fused
 //     mode.
 //   * Work items are visited chunk by chunk, tiles inside a chunk in groups of 4 tile
@@ -359,7 +360,7 @@ void tile_kernel(TileArgs a) {
         // arithmetic) instead of one load latency per output group.
         auto col_ok = [&](int nb) { return C::CW * wn + 32 * nb < cols; };
         auto row_ok = [&](int mb) { return C::RW * wm + 32 * mb < rows; };
-        if constexpr (MODE == kModeGelu) {
+        if constexpr (MODE == kModeLinear) {
             uint2 bb[NB][4];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -368,28 +369,31 @@ void tile_kernel(TileArgs a) {
                     const int nl = min(C::CW * wn + 32 * nb, cols - 32) + 8 * g + 4 * h;
                     bb[nb][g] = *reinterpret_cast<const uint2*>(a.bias + n0 + nl);
                 }
+            // bf16(act(T + bias)), the sum and the activation in fp32
+            auto store_all = [&](auto act) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
+                    for (int g = 0; g < 4; ++g)
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        if (!col_ok(nb) || !row_ok(mb)) continue;
-                        const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
-                        const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
-                        const f32x16& acc = T[nb][mb];
-                        const uint2 b = bb[nb][g];
-                        // bf16(gelu(T + bias)), the sum and gelu in fp32
-                        auto gq = [](float t, float bv) {
-                            return gelu_tanh_f32(__fadd_rn(t, bv));
-                        };
-                        const float g0 = gq(acc[4 * g], bf16_lo(b.x));
-                        const float g1 = gq(acc[4 * g + 1], bf16_hi(b.x));
-                        const float g2 = gq(acc[4 * g + 2], bf16_lo(b.y));
-                        const float g3 = gq(acc[4 * g + 3], bf16_hi(b.y));
-                        *reinterpret_cast<uint2*>(a.hout + m * a.N + n) =
-                            make_uint2(bf16x2_rne(g0, g1), bf16x2_rne(g2, g3));
-                    }
+                        for (int mb = 0; mb < MB; ++mb) {
+                            if (!col_ok(nb) || !row_ok(mb)) continue;
+                            const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
+                            const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
+                            const f32x16& acc = T[nb][mb];
+                            const uint2 b = bb[nb][g];
+                            const float g0 = act(__fadd_rn(acc[4 * g], bf16_lo(b.x)));
+                            const float g1 = act(__fadd_rn(acc[4 * g + 1], bf16_hi(b.x)));
+                            const float g2 = act(__fadd_rn(acc[4 * g + 2], bf16_lo(b.y)));
+                            const float g3 = act(__fadd_rn(acc[4 * g + 3], bf16_hi(b.y)));
+                            *reinterpret_cast<uint2*>(a.hout + m * a.N + n) =
+                                make_uint2(bf16x2_rne(g0, g1), bf16x2_rne(g2, g3));
+                        }
+            };
+            if (a.act == kActGeluTanh)
+                store_all([](float v) { return gelu_tanh_f32(v); });
+            else
+                store_all([](float v) { return v; });
         } else if constexpr (MODE == kModeFused) {
             uint2 bb[NB][4], rb[NB][4][MB];
 #pragma unroll
@@ -468,12 +472,12 @@ static hipError_t launch_tile_w(int mode, int bk, const TileArgs& a, int grid, h
     if (bk == 64) {
         if (mode == kModeFused) return launch_tile_t<kModeFused, 64, WT>(a, grid, s);
         if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64, WT>(a, grid, s);
-        if (mode == kModeGelu) return launch_tile_t<kModeGelu, 64, WT>(a, grid, s);
+        if (mode == kModeLinear) return launch_tile_t<kModeLinear, 64, WT>(a, grid, s);
         return launch_tile_t<kModePartials, 64, WT>(a, grid, s);
     }
     if (mode == kModeFused) return launch_tile_t<kModeFused, 32, WT>(a, grid, s);
     if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32, WT>(a, grid, s);
-    if (mode == kModeGelu) return launch_tile_t<kModeGelu, 32, WT>(a, grid, s);
+    if (mode == kModeLinear) return launch_tile_t<kModeLinear, 32, WT>(a, grid, s);
     return launch_tile_t<kModePartials, 32, WT>(a, grid, s);
 }
 
@@ -496,12 +500,12 @@ int tile_occupancy(int mode, int bk) {
     if (bk == 64) {
         if (mode == kModeFused) return occ_t<kModeFused, 64>();
         if (mode == kModeReduced) return occ_t<kModeReduced, 64>();
-        if (mode == kModeGelu) return occ_t<kModeGelu, 64>();
+        if (mode == kModeLinear) return occ_t<kModeLinear, 64>();
         return occ_t<kModePartials, 64>();
     }
     if (mode == kModeFused) return occ_t<kModeFused, 32>();
     if (mode == kModeReduced) return occ_t<kModeReduced, 32>();
-    if (mode == kModeGelu) return occ_t<kModeGelu, 32>();
+    if (mode == kModeLinear) return occ_t<kModeLinear, 32>();
     return occ_t<kModePartials, 32>();
 }
 

@@ -68,7 +68,8 @@
  * second stream of MMAR_SCHED_STREAMS waits for `stream` on entry and `stream` waits
  * for it before the call returns.
  *
- * Around the block: mmar_gelu_linear (the column-parallel MatMul + GeLU that produces the
+ * Around the block: mmar_linear / mmar_gelu_linear (the column-parallel MatMul + bias and
+ * GeLU, or no activation for an attention block's QKV projection, that produces the
  * block's X), mmar_unfused (the block one kernel per operation, for comparison) and
  * mmar_adam_step (the data-parallel gradient average + Adam step, one HBM pass).
  */
@@ -99,6 +100,9 @@ enum {
 };
 
 enum { MMAR_W_AUTO = -1, MMAR_W_DIRECT = 0, MMAR_W_PRETRANSPOSE = 1 };
+
+/* Activation of the producer MatMul (mmar_linear). */
+enum { MMAR_ACT_NONE = 0, MMAR_ACT_GELU_TANH = 1 };
 
 /* The fused block with the library's schedule for this shape: the plan set by
  * mmar_set_plan or found by mmar_autotune, else the persistent schedule.  chunk_m /
@@ -172,6 +176,15 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
  * workspace. */
 int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
                      int64_t M, int64_t N, int64_t K, void* stream);
+
+/* The producer MatMul with its activation chosen: MMAR_ACT_GELU_TANH is mmar_gelu_linear;
+ * MMAR_ACT_NONE gives H = X . W + bias, the QKV projection in front of an attention
+ * block's out-projection (its column block p holds the Q, K and V columns of the heads
+ * of rank p, which are what that rank's attention reads), rounded once from fp32 to bf16
+ * (nearest even).  Same arguments, preconditions and layout as mmar_gelu_linear; any
+ * other activation value returns MMAR_EINVAL before any device work. */
+int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
+                int64_t M, int64_t N, int64_t K, int32_t activation, void* stream);
 
 /* The data-parallel side of the CoCoNet record ("Key takeaways", fifth bullet: the
  * gradient ReduceScatter, the optimizer and the parameter AllGather fused) folded onto

@@ -1,5 +1,6 @@
-"""GPU parity of the producer MatMul (H = GeLU(X . W1 + b1), bf16) and of the MLP built
-from it and the block, through the C ABI, against the oracle.
+"""GPU parity of the producer MatMul (H = GeLU(X . W1 + b1), or H = X . W + b with no
+activation for an attention block's QKV projection, bf16) and of the MLP built from it
+and the block, through the C ABI, against the oracle.
 
 Bar for the bf16 H: every element equals the fp64 value rounded to bf16, except near a
 rounding midpoint (within the fp32 error bound), where either neighbour is accepted.
@@ -9,7 +10,7 @@ import pytest
 
 import oracle
 from oracle import producer
-from workload import WORKLOADS, make_producer_inputs, make_random_inputs
+from workload import WORKLOADS, make_producer_inputs, make_qkv_inputs, make_random_inputs
 from helpers import assert_within_tol, dev, host
 
 torch = pytest.importorskip("torch")
@@ -92,3 +93,51 @@ def test_producer_rejects_bad_arguments():
     mmar.gelu_linear(X, W, b, out=H)
     torch.cuda.synchronize()
     assert np.all(_h_bits(H) == 0)                # gelu(0) = 0
+
+
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_linear_without_activation_against_oracle(M, K, N):
+    print("linear none", M, K, N, flush=True)
+    inp = make_random_inputs(M, K, N, seed=M * 5 + N)
+    X, W, b = (dev(inp[k], torch) for k in ("X", "W", "bias"))
+    H = mmar.linear(X, W, b, "none")
+    torch.cuda.synchronize()
+    h, _, bound = producer.producer(inp["X"], inp["W"], inp["bias"], activation="none")
+    ties = producer.check_bf16_output(_h_bits(H), h, bound)
+    print("near-tie fraction", ties / (M * N), flush=True)
+    assert ties < 0.7 * M * N
+    # the GeLU mode of the same entry point gives gelu_linear's bits
+    Hg = mmar.linear(X, W, b, "gelu_tanh")
+    Hg2 = mmar.gelu_linear(X, W, b)
+    torch.cuda.synchronize()
+    assert np.array_equal(_h_bits(Hg), _h_bits(Hg2))
+
+
+def test_linear_qkv_full_size_sampled_rows():
+    """The GPT-2 attention block's QKV projection: [8192, 3072] x [3072, 9216], bias, no
+    activation."""
+    w = WORKLOADS["gpt2_attn"]
+    pin = make_qkv_inputs(w)
+    X0, Wq, bq = (dev(pin[k], torch) for k in ("X0", "Wqkv", "bqkv"))
+    H = mmar.linear(X0, Wq, bq, "none")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 8191], rng.choice(w.M, 60, replace=False)]))
+    h, _, bound = producer.producer(pin["X0"], pin["Wqkv"], pin["bqkv"], rows=rows, activation="none")
+    producer.check_bf16_output(_h_bits(H)[rows], h, bound)
+
+
+def test_linear_rejects_an_unknown_activation():
+    X = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((256, 64), dtype=torch.bfloat16, device="cuda")
+    b = torch.ones((64,), dtype=torch.bfloat16, device="cuda")
+    H = torch.full((64, 64), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        mmar.linear(X, W, b, "relu")
+    assert mmar.lib.mmar_linear(X.data_ptr(), W.data_ptr(), b.data_ptr(), H.data_ptr(),
+                                64, 64, 256, 5, None) == mmar.EINVAL
+    torch.cuda.synchronize()
+    assert np.all(host(H.float()) == 7.0)        # nothing was launched
+    mmar.linear(X, W, b, "none", out=H)
+    torch.cuda.synchronize()
+    assert np.all(host(H.float()) == 1.0)        # 0 + bias

@@ -116,6 +116,20 @@ def make_producer_inputs(w: Workload | str):
     return {"X0": X0, "W1": W1, "b1": b1, "M": w.M, "N": w.K, "K": w.N}
 
 
+def make_qkv_inputs(w: Workload | str):
+    """Inputs of the QKV projection in front of an attention block's out-projection:
+    X0 [M, N] (the hidden state), Wqkv [N, 3K] and bqkv [3K] (Q, K and V of K columns
+    each; the attention over them gives the block's X [M, K]).  Same recipe as
+    ``make_producer_inputs`` with seed = the workload's seed + 200."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng(w.seed + 200)
+    X0 = _draw(rng, (w.M, w.N), w.sigma_x)
+    Wqkv = _draw(rng, (w.N, 3 * w.K), w.sigma_w)
+    bqkv = _draw(rng, (3 * w.K,), w.sigma_bias)
+    return {"X0": X0, "Wqkv": Wqkv, "bqkv": bqkv, "M": w.M, "N": 3 * w.K, "K": w.N}
+
+
 @dataclasses.dataclass(frozen=True)
 class AdamWorkload:
     """A data-parallel optimizer step: n fp32 parameters, P replicas' gradients."""
