@@ -159,6 +159,38 @@ def run(X, W, bias, residual, P, p_drop, seed, rows=None, cols=None):
     return out, keep
 
 
+def error_bound_fp32(X, W, bias, residual, P, p_drop, keep, rows=None, cols=None):
+    """Per-element bound on |out_fp32 - out| for an fp32 computation of the block (slice
+    sums accumulated in fp32 from zero, reduced in fp32, fp32 epilogue), for the bf16
+    output variant: there the fp32 result is rounded once more, to bf16, and an element
+    may round either way only if out lies within this bound of a bf16 rounding midpoint.
+
+    With u = 2^-24 and mag = |X| . |W| + |bias| (fp64): 64 u scale mag (the summation
+    error, generous: an fp32 sum of n terms errs by about u sqrt(n) times its terms'
+    typical size, far below u times the sum of their magnitudes), plus 4 u (|v scale| +
+    |out|) for the bias add, the scale multiply and the residual add.  A dropped element
+    is the residual exactly (bound 0).  Parity unpinned beyond the fp32 simulations of the
+    tests: the pages fix no precision for the summation inside a slice."""
+    X = np.asarray(X)
+    W = np.asarray(W)
+    Xr = X if rows is None else X[np.asarray(rows)]
+    Wc = W if cols is None else W[:, np.asarray(cols)]
+    b = widen(bias) if cols is None else widen(np.asarray(bias)[cols])
+    res = np.asarray(residual)
+    res = res if rows is None else res[np.asarray(rows)]
+    res = res if cols is None else res[:, np.asarray(cols)]
+    scale = keep_scale(p_drop)
+    mag = np.abs(widen(Xr)) @ np.abs(widen(Wc)) + np.abs(b)[None, :]
+    v = None
+    for Sp in slice_partials(Xr, Wc, P):
+        v = Sp if v is None else v + Sp
+    v = (v + b[None, :]) * scale
+    out = widen(res) + v
+    u = 2.0 ** -24
+    bound = 64.0 * u * scale * mag + 4.0 * u * (np.abs(v) + np.abs(out))
+    return np.where(keep, bound, 0.0)
+
+
 def run_inputs(inp, rows=None, cols=None):
     """``run`` on a dict with keys X, W, bias, residual, P, p_drop, seed."""
     return run(inp["X"], inp["W"], inp["bias"], inp["residual"], inp["P"], inp["p_drop"],
