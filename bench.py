@@ -233,6 +233,11 @@ def main():
         t_tr = _ev_time(torch, lambda: mmar.transpose_weight(W, out=Wt), reps)[0]
         t_nt = _ev_time(torch, lambda: mmar.fused_nt(X, Wt, bias, res, P, p, seed, out=out), reps)[0]
         del Wt
+        # the same block with its output rounded once more, to bf16 (half the output bytes)
+        outb = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        t_bf16 = _ev_time(torch, lambda: mmar.fused_bf16(X, W, bias, res, P, p, seed, out=outb),
+                          reps)[0]
+        del outb
         del parts
         torch.cuda.empty_cache()
         # the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16) and the
@@ -295,7 +300,8 @@ def main():
                                "re_alone": t_re, "epi_alone": t_epi, "sequential": t_seq,
                                "streams": t_str, "unfused": t_unf, "persistent_w_direct": t_dir,
                                "persistent_w_pretranspose": t_pre, "w_transpose": t_tr,
-                               "persistent_w_given_transposed": t_nt}.items()}
+                               "persistent_w_given_transposed": t_nt,
+                               "fused_bf16_out": t_bf16}.items()}
         result["fused_us_stats"] = {"median": round(t_fused * 1e3, 2), "min": round(t_fused_min * 1e3, 2),
                                     "p90": round(t_fused_p90 * 1e3, 2),
                                     "median_cold_caches": round(t_cold * 1e3, 2)}

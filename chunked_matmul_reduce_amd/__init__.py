@@ -9,6 +9,7 @@ Block computed (see include/mmar.h for the full contract):
     out = residual + dropout_p(bias + sum_p X[:, K_p] @ W[K_p, :])     (fp32 out)
 with bf16 X [M,K], W [K,N], bias [N], residual [M,N]; P equal K-slices; fp32 slice
 accumulation from zero; fixed-order fp32 reduction; counter-based Philox4x32-10 mask.
+``fused_bf16`` is the same block with its output rounded once more, to bf16.
 Around it: ``linear`` / ``gelu_linear`` / ``mlp`` (the producer MatMul + bias and GeLU,
 or no activation for an attention block's QKV projection, in front of the block),
 ``unfused`` (the block one kernel per operation) and ``adam_step`` (the data-parallel
@@ -40,6 +41,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "mmar_fused": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_fused_nt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
+    "mmar_fused_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _P]),
     "mmar_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32]),
     "mmar_fused_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32,
                                      _I32, _I32, _I32, _P, _SZ, _P]),
@@ -181,6 +183,23 @@ def fused(X, W, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, stream=
                             _bits(residual, "residual", (M, N)), out.data_ptr(), M, N, K, int(P),
                             float(p_drop), int(seed) & (2 ** 64 - 1), int(chunk[0]), int(chunk[1]),
                             _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def fused_bf16(X, W, bias, residual, P, p_drop, seed, out=None, stream=None):
+    """mmar_fused_bf16: the block with its fp32 result rounded once to bf16; returns bf16
+    out [M, N]."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, P)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    op = _bits(out, "out", (M, N))
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_fused_bf16(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)),
+                                 _bits(bias, "bias", (N,)), _bits(residual, "residual", (M, N)),
+                                 op, M, N, K, int(P), float(p_drop), int(seed) & (2 ** 64 - 1),
+                                 _stream(X.device, stream))
     _check(rc)
     return out
 

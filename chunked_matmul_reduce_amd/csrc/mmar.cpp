@@ -364,14 +364,18 @@ Plan plan_for(const DevState* st, const Shape& s, int32_t sched, int32_t cm, int
 }
 
 // ------------------------------------------------------------------ runners
+// Every member starts zeroed / null: a null hout keeps the fused mode's fp32 output.
 struct Call {
-    const uint16_t *X, *W, *bias, *residual;
-    float* out;
-    uint16_t* hout;   // bf16 output of the producer MatMul
-    int act;          // its activation (mmar::Activation)
-    Shape s;
-    DropParams drop;
-    bool w_t;   // W holds W^T [N, K]
+    const uint16_t* X = nullptr;
+    const uint16_t* W = nullptr;
+    const uint16_t* bias = nullptr;
+    const uint16_t* residual = nullptr;
+    float* out = nullptr;
+    uint16_t* hout = nullptr;   // bf16 output (producer MatMul; fused block's bf16 variant)
+    int act = 0;                // the producer's activation (mmar::Activation)
+    Shape s{};
+    DropParams drop{};
+    bool w_t = false;           // W holds W^T [N, K]
 };
 
 // K step of the tile kernel: 64 when it divides K/P, else 32.  MMAR_FORCE_BK=32 selects
@@ -657,6 +661,37 @@ int mmar_fused_nt(const uint16_t* X, const uint16_t* Wt, const uint16_t* bias,
                       MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_DIRECT, nullptr, 0, stream);
 }
 
+int mmar_fused_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                    const uint16_t* residual, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                    int32_t P, float p_drop, uint64_t seed, void* stream) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    int rc;
+    if ((rc = check_shape(s))) return rc;
+    if ((rc = check_ptr(X, "X")) || (rc = check_ptr(W, "W")) || (rc = check_ptr(bias, "bias")) ||
+        (rc = check_ptr(residual, "residual")) || (rc = check_ptr(out, "out")))
+        return rc;
+    const size_t ob = static_cast<size_t>(M * N) * 2;
+    if (overlaps(out, ob, X, static_cast<size_t>(M * K) * 2) ||
+        overlaps(out, ob, W, static_cast<size_t>(K * N) * 2) ||
+        overlaps(out, ob, bias, static_cast<size_t>(N) * 2) ||
+        overlaps(out, ob, residual, static_cast<size_t>(M * N) * 2))
+        return fail(MMAR_EINVAL, "out overlaps an input");
+    Call c;
+    if ((rc = drop_params(p_drop, seed, &c.drop))) return rc;
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    c.X = X;
+    c.W = W;
+    c.bias = bias;
+    c.residual = residual;
+    c.hout = out;
+    c.s = s;
+    c.w_t = false;
+    return run_persistent(st, c, mmar::kModeFused, static_cast<int>(M), static_cast<int>(N),
+                          static_cast<hipStream_t>(stream));
+}
+
 size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, int32_t P,
                             int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode) {
     g_err.clear();
@@ -731,7 +766,6 @@ int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     Call c;
-    std::memset(&c, 0, sizeof c);
     c.X = X;
     c.W = W;
     c.out = T_out;
@@ -757,7 +791,6 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     Call c;
-    std::memset(&c, 0, sizeof c);
     c.X = X;
     c.W = W;
     c.out = partials;
@@ -843,7 +876,6 @@ int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     Call c;
-    std::memset(&c, 0, sizeof c);
     c.X = X;
     c.W = W;
     c.bias = bias;

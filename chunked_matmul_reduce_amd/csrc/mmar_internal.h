@@ -41,7 +41,8 @@ struct TileArgs {
     const uint16_t* bias;
     const uint16_t* residual;
     float* out;          // kModeFused / kModeReduced: [M, N]
-    uint16_t* hout;      // kModeLinear: bf16 [M, N]
+    uint16_t* hout;      // kModeLinear: bf16 [M, N]; kModeFused: bf16 output instead of out
+                         // when set
     float* ws;           // kModePartials: [P][RM][RN] for the region
     int64_t M, N, K;
     int32_t P, Ks;       // Ks = K / P

@@ -410,22 +410,31 @@ void tile_kernel(TileArgs a) {
                             a.residual + (static_cast<int64_t>(m0) + ml) * a.N + n0 + nl);
                     }
                 }
+            // the output as fp32, or rounded once more to bf16 (nearest even) when hout is set
+            auto store_all = [&](auto store) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+                for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int g = 0; g < 4; ++g)
+                    for (int g = 0; g < 4; ++g)
 #pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        if (!col_ok(nb) || !row_ok(mb)) continue;
-                        const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
-                        const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
-                        const f32x16& acc = T[nb][mb];
-                        const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
-                                                     acc[4 * g + 3]);
-                        const int64_t e = m * a.N + n;
-                        *reinterpret_cast<float4*>(a.out + e) =
-                            epilogue4(v, bb[nb][g], rb[nb][g][mb], e, a.drop);
-                    }
+                        for (int mb = 0; mb < MB; ++mb) {
+                            if (!col_ok(nb) || !row_ok(mb)) continue;
+                            const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
+                            const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
+                            const f32x16& acc = T[nb][mb];
+                            const float4 v = make_float4(acc[4 * g], acc[4 * g + 1],
+                                                         acc[4 * g + 2], acc[4 * g + 3]);
+                            const int64_t e = m * a.N + n;
+                            store(e, epilogue4(v, bb[nb][g], rb[nb][g][mb], e, a.drop));
+                        }
+            };
+            if (a.hout)
+                store_all([&](int64_t e, float4 o) {
+                    *reinterpret_cast<uint2*>(a.hout + e) =
+                        make_uint2(bf16x2_rne(o.x, o.y), bf16x2_rne(o.z, o.w));
+                });
+            else
+                store_all([&](int64_t e, float4 o) { *reinterpret_cast<float4*>(a.out + e) = o; });
         } else {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)

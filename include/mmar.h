@@ -120,6 +120,19 @@ int mmar_fused_nt(const uint16_t* X, const uint16_t* Wt, const uint16_t* bias,
                   int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                   void* stream);
 
+/* The block with a bf16 output, for a model that keeps its residual stream in bf16: out
+ * [M,N] bf16 row-major (written; must not overlap an input) receives the fp32 result of
+ * mmar_fused rounded once to bf16 (nearest even), so each element equals that rounding of
+ * mmar_fused's output on the same arguments.  The fp32 tolerance of the block does not
+ * carry over (the bf16 rounding alone exceeds it); the result is judged against the
+ * oracle's fp64 value rounded to bf16, either neighbour accepted where that value lies
+ * within the fp32 error bound of a rounding midpoint.  Persistent schedule, W as
+ * [K,N], whole output in one chunk; preconditions, dropout and errors as mmar_fused.  No
+ * workspace. */
+int mmar_fused_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                    const uint16_t* residual, uint16_t* out, int64_t M, int64_t N, int64_t K,
+                    int32_t P, float p_drop, uint64_t seed, void* stream);
+
 /* Workspace bytes a plan needs: K N 2 (256-aligned) for MMAR_W_PRETRANSPOSE, plus the
  * partial-product ring for MMAR_SCHED_SEQUENTIAL (P chunk_m chunk_n 4) and
  * MMAR_SCHED_STREAMS (ring times that).  schedule AUTO: the plan mmar_fused would use

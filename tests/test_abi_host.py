@@ -91,6 +91,11 @@ def test_other_entry_points_validate():
              None) == mmar.EALIGN
     assert L.mmar_gelu_linear(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 64, 250, None) == mmar.EINVAL
     assert L.mmar_gelu_linear(FAKE, FAKE * 2, FAKE * 3, FAKE, 64, 64, 256, None) == mmar.EINVAL
+    FB = L.mmar_fused_bf16
+    assert FB(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 4, 64, 256, 256, 4, 0.1, 1, None) == mmar.EINVAL
+    assert FB(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 250, 4, 0.1, 1, None) == mmar.EINVAL
+    assert FB(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, -0.5, 1, None) == mmar.EINVAL
+    assert FB(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64 + 4, 64, 256, 256, 4, 0.1, 1, None) == mmar.EALIGN
     assert L.mmar_linear(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 64, 256, 2, None) == mmar.EINVAL
     assert L.mmar_linear(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 64, 256, -1, None) == mmar.EINVAL
     assert L.mmar_linear(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 64, 250, 0, None) == mmar.EINVAL
