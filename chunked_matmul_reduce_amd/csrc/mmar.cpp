@@ -466,7 +466,7 @@ int launch_reduce(const DevState* st, const float* ws, const uint16_t* bias,
     const int64_t groups = static_cast<int64_t>(RM) * (RN / 4);
     int occ = std::max(1, st->red_occ);
     int64_t grid = std::min<int64_t>((groups + 255) / 256, static_cast<int64_t>(st->cus) * occ * 2);
-    MMAR_HIP(mmar::launch_reduce_epilogue(r, static_cast<int>(std::max<int64_t>(1, grid)), 0, s));
+    MMAR_HIP(mmar::launch_reduce_epilogue(r, static_cast<int>(std::max<int64_t>(1, grid)), s));
     return MMAR_OK;
 }
 

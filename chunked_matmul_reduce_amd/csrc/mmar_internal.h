@@ -84,10 +84,7 @@ constexpr int kThreads = 256;
 // holds W^T [N, K] instead of W [K, N].
 hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, hipStream_t s);
 hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, hipStream_t s);
-// lds_bytes: dynamic LDS the reduce+epilogue workgroups reserve (unused by the kernel);
-// a workgroup that asks for any cannot share a CU with a tile-kernel workgroup (which
-// holds the whole LDS), so it runs only on CUs the tile kernel left free.
-hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, int lds_bytes, hipStream_t s);
+hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s);
 hipError_t launch_adam(const AdamArgs& a, int grid, hipStream_t s);
 // The unfused tail (unfused.hip): sum of the P partials ws [P][M][N] into T (may alias ws),
