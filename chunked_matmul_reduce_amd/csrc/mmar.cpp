@@ -48,6 +48,7 @@ struct Plan {
     int sched = MMAR_SCHED_PERSISTENT;
     int cm = 0, cn = 0, ring = 0;
     int wmode = MMAR_W_AUTO;   // MMAR_W_DIRECT or MMAR_W_PRETRANSPOSE once resolved
+    int hm = 0, hn = 0;        // MMAR_SCHED_BALANCED: head block [0, hm) x [0, hn) (0: none)
 };
 
 constexpr int kMaxRing = 8;
@@ -105,7 +106,7 @@ int check_chunk(const Shape& s, int32_t cm, int32_t cn) {
 }
 
 int check_sched(int32_t sched, int32_t ring, int32_t wmode) {
-    if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_PERSISTENT)
+    if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_BALANCED)
         return fail(MMAR_EINVAL, "unknown schedule");
     if (ring < 0 || ring > kMaxRing) return fail(MMAR_EINVAL, "ring must be in [0, 8]");
     if (wmode < MMAR_W_AUTO || wmode > MMAR_W_PRETRANSPOSE)
@@ -214,7 +215,40 @@ int ensure_streams(DevState* st) {
 // measured shapes the in-kernel read wins (the autotuner can still pick the other).
 int default_wmode(const Shape&) { return MMAR_W_DIRECT; }
 
-Plan default_plan(const Shape& s) {
+constexpr int kDefaultCUs = 256;   // MI355X; used where no device has been seen yet
+
+int64_t tile_count(int64_t rows, int64_t cols) {
+    return ((rows + mmar::kBM - 1) / mmar::kBM) * ((cols + mmar::kBN - 1) / mmar::kBN);
+}
+
+// Head of the balanced schedule: the largest block of whole leading tile columns
+// [0, M) x [0, hn), or of whole leading tile rows [0, hm) x [0, N), whose tile count is a
+// positive multiple of g (the persistent grid, one workgroup per CU), leaving a non-empty
+// tail.  No split ({0, 0}) when the tile count already is a multiple of g or none exists.
+std::pair<int, int> balanced_split(const Shape& s, int g) {
+    std::pair<int, int> best{0, 0};
+    if (g < 1 || tile_count(s.M, s.N) % g == 0) return best;
+    const int64_t tm = (s.M + mmar::kBM - 1) / mmar::kBM, tn = (s.N + mmar::kBN - 1) / mmar::kBN;
+    int64_t best_head = 0;
+    for (int64_t j = tn - 1; j >= 1; --j)
+        if (tm * j >= g && (tm * j) % g == 0) {
+            best_head = tm * j;
+            best = {static_cast<int>(s.M), static_cast<int>(j * mmar::kBN)};
+            break;
+        }
+    for (int64_t i = tm - 1; i >= 1; --i)
+        if (i * tn >= g && (i * tn) % g == 0) {
+            if (i * tn > best_head) best = {static_cast<int>(i * mmar::kBM), static_cast<int>(s.N)};
+            break;
+        }
+    return best;
+}
+
+// The default plan is the persistent schedule.  The balanced schedule is left to the
+// autotuner: on the BERT-shaped block (640 tiles: two full rounds and a half one) it ran
+// as fast as the persistent schedule, whose half-empty last round runs faster than a
+// full one, not half a round faster.
+Plan default_plan(const Shape& s, int) {
     Plan p;
     p.sched = MMAR_SCHED_PERSISTENT;
     p.cm = static_cast<int>(s.M);
@@ -224,9 +258,20 @@ Plan default_plan(const Shape& s) {
     return p;
 }
 
-// Fill in zero chunk sizes, ring and weight mode.
-Plan resolve(const Shape& s, Plan p) {
+// Fill in zero chunk sizes, ring, weight mode and the balanced schedule's head.
+Plan resolve(const Shape& s, Plan p, int cus) {
+    p.hm = p.hn = 0;
     if (p.sched == MMAR_SCHED_AUTO) p.sched = MMAR_SCHED_PERSISTENT;
+    if (p.sched == MMAR_SCHED_BALANCED) {
+        p.cm = static_cast<int>(s.M);
+        p.cn = static_cast<int>(s.N);
+        p.ring = 0;
+        const auto sp = balanced_split(s, cus);
+        p.hm = sp.first;
+        p.hn = sp.second;
+        if (p.wmode == MMAR_W_AUTO) p.wmode = default_wmode(s);
+        return p;
+    }
     if (p.sched == MMAR_SCHED_STREAMS) {
         if (p.cm == 0) {
             // about 8 chunks of whole rows by default
@@ -259,6 +304,12 @@ size_t wt_bytes_for(const Shape& s, const Plan& p, bool w_given_t) {
 }
 
 size_t ring_bytes_for(const Shape& s, const Plan& p) {
+    if (p.sched == MMAR_SCHED_BALANCED) {   // the tail's partials
+        if (p.hm == 0) return 0;
+        const size_t tail = static_cast<size_t>(s.M) * static_cast<size_t>(s.N) -
+                            static_cast<size_t>(p.hm) * static_cast<size_t>(p.hn);
+        return align_up(static_cast<size_t>(s.P) * tail * sizeof(float));
+    }
     const size_t slot = static_cast<size_t>(s.P) * static_cast<size_t>(p.cm) *
                         static_cast<size_t>(p.cn) * sizeof(float);
     if (p.sched == MMAR_SCHED_SEQUENTIAL) return align_up(slot);
@@ -279,7 +330,8 @@ bool plan_is_valid(const Shape& s, const Plan& p) {
     const bool chunk_ok = p.cm > 0 && p.cn > 0 && p.cm % 32 == 0 && p.cn % 32 == 0 &&
                           s.M % p.cm == 0 && s.N % p.cn == 0;
     const bool sched_ok = p.sched == MMAR_SCHED_SEQUENTIAL || p.sched == MMAR_SCHED_STREAMS ||
-                          p.sched == MMAR_SCHED_PERSISTENT;
+                          p.sched == MMAR_SCHED_PERSISTENT ||
+                          (p.sched == MMAR_SCHED_BALANCED && p.cm == s.M && p.cn == s.N);
     const bool ring_ok = p.ring >= 0 && p.ring <= kMaxRing &&
                          (p.sched != MMAR_SCHED_STREAMS || p.ring >= 1);
     const bool w_ok = p.wmode == MMAR_W_DIRECT || p.wmode == MMAR_W_PRETRANSPOSE;
@@ -341,7 +393,7 @@ Plan lookup_plan(const DevState* st, const Shape& s) {
     std::lock_guard<std::mutex> lk(g_mu);
     load_plan_cache_locked();
     auto it = g_plans.find(PlanKey(st->arch, s.M, s.N, s.K, s.P));
-    return it == g_plans.end() ? default_plan(s) : it->second;
+    return it == g_plans.end() ? default_plan(s, st->cus) : it->second;
 }
 
 // Plan for a call: the cached / default plan (schedule AUTO) or the explicit arguments,
@@ -360,7 +412,7 @@ Plan plan_for(const DevState* st, const Shape& s, int32_t sched, int32_t cm, int
     if (cn) p.cn = cn;
     if (ring) p.ring = ring;
     if (wmode != MMAR_W_AUTO) p.wmode = wmode;
-    return resolve(s, p);
+    return resolve(s, p, st->cus);
 }
 
 // ------------------------------------------------------------------ runners
@@ -512,6 +564,26 @@ int run_chunked(DevState* st, const Call& c, const Plan& p, float* ws, hipStream
     return MMAR_OK;
 }
 
+// Balanced schedule: the persistent kernel over the head block (whole rounds), then the
+// tail's one-slice partials spread over every CU and the reduce+epilogue kernel over the
+// tail; the same bits as the persistent schedule (the same MFMA sequence per slice, the
+// same fixed-order fp32 reduction and epilogue).
+int run_balanced(const DevState* st, const Call& c, const Plan& p, float* ws, hipStream_t s) {
+    if (p.hm == 0) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s);
+    const int M = static_cast<int>(c.s.M), N = static_cast<int>(c.s.N);
+    const int bk = bk_for(c.s);
+    TileArgs a = tile_args(c, 0, 0, p.hm, p.hn, p.hm, p.hn);
+    a.total_items = static_cast<int32_t>(tiles_in(p.hm, p.hn));
+    MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, a,
+                               grid_for(st, mmar::kModeFused, bk, a.total_items), s));
+    const int tr0 = p.hm == M ? 0 : p.hm, tc0 = p.hm == M ? p.hn : 0;
+    const int TM = M - tr0, TN = N - tc0;
+    int rc = launch_partials(st, c, tr0, tc0, TM, TN, ws, s);
+    if (rc) return rc;
+    return launch_reduce(st, ws, c.bias, c.residual, c.out, c.s.N, c.s.P, tr0, tc0, TM, TN,
+                         c.drop, s);
+}
+
 // What a call runs: the fused block (any schedule), or the measurement paths that share
 // its kernels.
 enum RunKind { kRunFused = 0, kRunReduced = 1, kRunPartials = 2 };
@@ -530,6 +602,8 @@ int run_with_ws(DevState* st, Call c, const Plan& p, RunKind kind, char* ws, hip
         return launch_partials(st, c, 0, 0, static_cast<int>(c.s.M), static_cast<int>(c.s.N),
                                c.out, s);
     if (p.sched == MMAR_SCHED_PERSISTENT) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s);
+    if (p.sched == MMAR_SCHED_BALANCED)
+        return run_balanced(st, c, p, reinterpret_cast<float*>(ws + wt_bytes), s);
     return run_chunked(st, c, p, reinterpret_cast<float*>(ws + wt_bytes), s);
 }
 
@@ -597,6 +671,8 @@ int fused_impl(const uint16_t* X, const uint16_t* W, bool w_t, const uint16_t* b
     int rc = check_call(X, W, bias, residual, out, s, p_drop, seed, chunk_m, chunk_n, &c);
     if (rc) return rc;
     if ((rc = check_sched(sched, ring, wmode))) return rc;
+    if (sched == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
+        return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
     c.w_t = w_t;
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
@@ -698,20 +774,32 @@ size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, i
     const Shape s{M, N, K, P};
     if (check_shape(s) || check_chunk(s, chunk_m, chunk_n) || check_sched(schedule, ring, w_mode))
         return 0;
+    if (schedule == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N))) {
+        fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
+        return 0;
+    }
+    // the current device's architecture and CU count if the library has seen it
+    std::string ws_arch = "gfx950";
+    int ws_cus = kDefaultCUs;
+    {
+        int dev = -1;
+        if (hipGetDevice(&dev) == hipSuccess) {
+            std::lock_guard<std::mutex> lk(g_mu);
+            auto it = g_dev.find(dev);
+            if (it != g_dev.end()) {
+                ws_arch = it->second->arch;
+                ws_cus = it->second->cus;
+            }
+        } else {
+            (void)hipGetLastError();
+        }
+    }
     Plan p;
     if (schedule == MMAR_SCHED_AUTO) {
         std::lock_guard<std::mutex> lk(g_mu);
         load_plan_cache_locked();
-        int dev = -1;
-        std::string arch = "gfx950";
-        if (hipGetDevice(&dev) == hipSuccess) {
-            auto it = g_dev.find(dev);
-            if (it != g_dev.end()) arch = it->second->arch;
-        } else {
-            (void)hipGetLastError();
-        }
-        auto pit = g_plans.find(PlanKey(arch, M, N, K, P));
-        p = pit == g_plans.end() ? default_plan(s) : pit->second;
+        auto pit = g_plans.find(PlanKey(ws_arch, M, N, K, P));
+        p = pit == g_plans.end() ? default_plan(s, ws_cus) : pit->second;
     } else {
         p.sched = schedule;
         p.ring = ring;
@@ -721,7 +809,7 @@ size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, i
     if (chunk_n) p.cn = chunk_n;
     if (ring) p.ring = ring;
     if (w_mode != MMAR_W_AUTO) p.wmode = w_mode;
-    return ws_bytes_for(s, resolve(s, p), false);
+    return ws_bytes_for(s, resolve(s, p, ws_cus), false);
 }
 
 int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
@@ -952,6 +1040,8 @@ int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
     if ((rc = check_shape(s)) || (rc = check_chunk(s, chunk_m, chunk_n)) ||
         (rc = check_sched(schedule, ring, w_mode)))
         return rc;
+    if (schedule == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
+        return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     std::lock_guard<std::mutex> lk(g_mu);
@@ -967,7 +1057,7 @@ int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
     p.cn = chunk_n;
     p.ring = ring;
     p.wmode = w_mode;
-    g_plans[key] = resolve(s, p);
+    g_plans[key] = resolve(s, p, st->cus);
     return MMAR_OK;
 }
 
@@ -981,7 +1071,7 @@ int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
         return fail(MMAR_EINVAL, "NULL output pointer");
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
-    const Plan p = resolve(s, lookup_plan(st, s));
+    const Plan p = resolve(s, lookup_plan(st, s), st->cus);
     *schedule = p.sched;
     *chunk_m = p.cm;
     *chunk_n = p.cn;
@@ -1010,6 +1100,13 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
                 p.wmode = wm;
                 cands.push_back(p);
             }
+    if (balanced_split(s, st->cus).first != 0)
+        for (int wm : {MMAR_W_DIRECT, MMAR_W_PRETRANSPOSE}) {
+            Plan p;
+            p.sched = MMAR_SCHED_BALANCED;
+            p.wmode = wm;
+            cands.push_back(p);
+        }
     if (flags & 1u) {
         for (int cm : divisors32(M, {2, 4, 8, 16}))
             for (int r : {2, 3}) {
@@ -1067,7 +1164,7 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
     Plan best;
     float best_ms = 1e30f;
     for (Plan p : cands) {
-        p = resolve(s, p);
+        p = resolve(s, p, st->cus);
         float ms = 0;
         rc = time_plan(st, c, p, stream, &ms);
         if (rc) {

@@ -32,6 +32,15 @@
  *   MMAR_SCHED_PERSISTENT  one persistent kernel: each workgroup walks output tiles in
  *                          chunk order, reduces the P slices of a tile in registers and
  *                          applies the epilogue before moving on; no partials reach HBM.
+ *   MMAR_SCHED_BALANCED    PERSISTENT over a head block of whole tile columns (or rows)
+ *                          whose tile count is a multiple of the device's CU count, so
+ *                          every round of the persistent grid is full; the tail, whose
+ *                          tiles would leave part of the last round idle, is split by
+ *                          slice instead: its P one-slice partials per tile are spread
+ *                          over all CUs, then the reduce+epilogue kernel sums them in
+ *                          slice order.  Whole-output chunk only; the tail's partials
+ *                          take P x M x (tail columns) x 4 bytes (or P x (tail rows) x
+ *                          N x 4) of workspace.  Without such a split it is PERSISTENT.
  *
  * Layouts.  X [M,K], W [K,N], residual [M,N] row-major, contiguous, bf16 bit patterns
  * (uint16); bias [N] bf16 bits; out [M,N] row-major fp32.  All tensor pointers are
@@ -96,7 +105,8 @@ enum {
     MMAR_SCHED_AUTO = 0,
     MMAR_SCHED_SEQUENTIAL = 1,
     MMAR_SCHED_STREAMS = 2,
-    MMAR_SCHED_PERSISTENT = 3
+    MMAR_SCHED_PERSISTENT = 3,
+    MMAR_SCHED_BALANCED = 4
 };
 
 enum { MMAR_W_AUTO = -1, MMAR_W_DIRECT = 0, MMAR_W_PRETRANSPOSE = 1 };

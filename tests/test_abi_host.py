@@ -105,6 +105,22 @@ def test_other_entry_points_validate():
     assert L.mmar_autotune(64, 256, 250, 4, 0) == mmar.EINVAL
 
 
+def test_balanced_schedule_workspace_and_chunk():
+    """The balanced schedule's tail partials: P x M x (tail columns) x 4 bytes, or
+    P x (tail rows) x N x 4; none when the tile count is already a multiple of 256."""
+    assert mmar.workspace_bytes("balanced", 8192, 2560, 10240, 8) == 8 * 8192 * 512 * 4
+    assert mmar.workspace_bytes("auto", 8192, 2560, 10240, 8) == 0     # default: persistent
+    assert mmar.workspace_bytes("balanced", 8192, 3072, 12288, 16) == 0
+    assert mmar.workspace_bytes("balanced", 2080, 4096, 512, 4) == 4 * 32 * 4096 * 4
+    assert mmar.workspace_bytes("balanced", 8192, 1088, 512, 4) == 4 * 8192 * 64 * 4
+    assert mmar.workspace_bytes("balanced", 64, 256, 256, 4) == 0          # one tile
+    with pytest.raises(mmar.MmarError):
+        mmar.workspace_bytes("balanced", 8192, 2560, 10240, 8, chunk=(4096, 0))
+    L = mmar.lib
+    assert L.mmar_set_plan(8192, 2560, 10240, 8, 4, 4096, 0, 0, -1) == mmar.EINVAL
+    assert L.mmar_workspace_bytes(5, 8192, 2560, 10240, 8, 0, 0, 0, -1) == 0
+
+
 def test_workspace_bytes():
     wt = 12288 * 3072 * 2   # pre-transposed weight of the 8192-row block
     assert mmar.workspace_bytes("persistent", 8192, 3072, 12288, 16) == 0

@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # collected on CPU-only machines, never run t
 import chunked_matmul_reduce_amd as mmar  # noqa: E402
 
 ONE = 0x3F80
-SCHEDS = ["persistent", "sequential", "streams"]
+SCHEDS = ["persistent", "sequential", "streams", "balanced"]   # balanced: whole-output chunk only
 
 
 def _to_dev(inp):
@@ -70,6 +70,8 @@ def test_tiny_all_schedules_chunks_bit_identical():
     outs = {}
     for sched in SCHEDS:
         for chunk in [(32, 64), (64, 64), (32, 256), (64, 256), (0, 0)]:
+            if sched == "balanced" and chunk != (0, 0):
+                continue
             for wm in ("direct", "pretranspose"):
                 out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, w_mode=wm)
                 outs[(sched, chunk, wm)] = out
@@ -101,6 +103,8 @@ def test_ragged_shapes_against_oracle(M, K, N, P):
     ref = None
     for sched in SCHEDS:
         for chunk in [(0, 0), (32, 32), (M // 2 if (M // 2) % 32 == 0 else M, N)]:
+            if sched == "balanced" and chunk != (0, 0):
+                continue
             for wm in ("direct", "pretranspose"):
                 out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk, w_mode=wm)
                 _check_block(inp, out)
@@ -154,6 +158,33 @@ def test_full_size_schedule_invariance():
                                    ("sequential", (0, 0), 0, "direct")]:
         out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, ring, w_mode=wm)
         assert np.array_equal(f32_bits(out), ref), (sched, chunk, ring, wm)
+
+
+# (M, K, N, P) with a head of whole rounds on 256 CUs and a tail: one ragged tile column,
+# one ragged tile row, and the BERT-shaped block (512 + 128 tiles)
+BALANCED_SPLITS = [(8192, 512, 1088, 4), (2080, 512, 4096, 4), (8192, 10240, 2560, 8)]
+
+
+@pytest.mark.parametrize("M,K,N,P", BALANCED_SPLITS)
+def test_balanced_split_bits_and_oracle(M, K, N, P):
+    """The balanced schedule (persistent head, tail by slice through partials and the
+    reduce+epilogue kernel) gives the persistent schedule's bits; sampled rows, the tail
+    included, against the oracle."""
+    print("balanced", M, K, N, P, flush=True)
+    assert mmar.workspace_bytes("balanced", M, N, K, P) > 0      # the split exists
+    inp = make_random_inputs(M, K, N, seed=M + N + P)
+    inp.update(M=M, K=K, N=N, P=P, p_drop=np.float32(0.1), seed=(N << 20) + M)
+    d = _to_dev(inp)
+    ref = _run(d, P, inp["p_drop"], inp["seed"], "persistent", w_mode="direct")
+    for wm in ("direct", "pretranspose"):
+        out = _run(d, P, inp["p_drop"], inp["seed"], "balanced", w_mode=wm)
+        assert np.array_equal(f32_bits(out), f32_bits(ref)), wm
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 33, M - 32, M - 1],
+                                     rng.choice(M, 40, replace=False)]))
+    print("max rel err on sampled rows", _check_block(inp, out, rows=rows), flush=True)
+    del d
+    torch.cuda.empty_cache()
 
 
 # ---------------------------------------------------------------- structure pins
