@@ -11,8 +11,8 @@
 // X in the B slot), so that a lane's accumulator holds one output row and, per group of
 // four registers, four consecutive columns: exactly one Philox group, one 8-byte bias /
 // residual load and one 16-byte fp32 store, with no cross-lane exchange.
-//   * Staging: global_load_lds_dwordx4 copies (HBM/L2 -> LDS, no register round trip)
-//     into a ring of X stages [256][BK] and a ring of W stages [BK][128] (W^T [128][BK]
+//   * Staging: global_load_lds_dwordx4 copies (HBM/L2 -> LDS, no register round trip),
+//     issued in pairs that share one M0 setting, into a ring of X stages [256][BK] and a ring of W stages [BK][128] (W^T [128][BK]
 //     when W is given transposed), LEAD K steps ahead; 16-byte chunks are XOR-swizzled
 //     so the copies and the operand reads are bank-conflict free.  W [K, N] operands are
 //     read with the LDS transpose read ds_read_b64_tr_b16, everything else with 16-byte
@@ -81,6 +81,7 @@ struct TileCfg {
     static constexpr int LDS_BYTES = (XSTAGES * XS + WSTAGES * WS) * 2;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
     static_assert(MB * NB == 8, "8 MFMA blocks per wave");
+    static_assert(XQ % 2 == 0 && WQ % 2 == 0, "copies go in pairs");
 };
 
 // 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).
@@ -93,21 +94,28 @@ __device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
 // s_waitcnt on the vector-memory counter only (gfx9 encoding).
 #define MMAR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
 
-// One 16-byte global -> LDS copy per lane from sbase + voff (sbase wave-uniform, voff a
-// per-lane byte offset); lane l's bytes land at lds_addr + 16 l (lds_addr wave-uniform,
-// passed in M0, which is saved and restored).  Inline asm, so that the compiler does not
-// turn its LDS write into a wait on every later LDS read; the kernel waits on the
-// vector-memory counter itself.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+// Two 16-byte global -> LDS copies per lane with one M0 setting (sbase wave-uniform in
+// SGPRs, voff0 / voff1 per-lane byte offsets, lds_addr1 wave-uniform): copy 0 reads
+// sbase + voff0 - 1024 and lands at lds_addr1 - 1024 + 16 lane, copy 1 reads
+// sbase + voff1 and lands at lds_addr1 + 16 lane.  The instruction offset applies to both
+// addresses, so voff0 holds its byte offset plus 1024 (no wrap: an offset within a tile
+// of X, W or W^T, each under 2^31 elements, stays far below 2^32 - 1024).  M0 is saved and
+// restored.  Inline asm, so that the compiler does not turn
+// the LDS writes into a wait on every later LDS read; the kernel waits on the
+// vector-memory counter itself.  One M0 setting per pair instead of per copy takes 30 of
+// the about 230 instructions a wave issues per 64-deep K step.
+__device__ __forceinline__ void dma16x2(const void* sbase, uint32_t voff0, uint32_t voff1,
+                                        uint32_t lds_addr1) {
     uint32_t saved;
     asm volatile(
         "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
+        "s_mov_b32 m0, %4\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
+        "global_load_lds_dwordx4 %1, %3 offset:-1024\n\t"
+        "global_load_lds_dwordx4 %2, %3\n\t"
         "s_mov_b32 m0, %0"
         : "=&s"(saved)
-        : "v"(voff), "s"(sbase), "s"(lds_addr)
+        : "v"(voff0), "v"(voff1), "s"(sbase), "s"(lds_addr1)
         : "memory");
 }
 
@@ -192,7 +200,8 @@ void tile_kernel(TileArgs a) {
             const int idx = 64 * (C::XQ * wave + q) + lane;
             const int r = idx / C::CPR, pos = idx % C::CPR;
             const int c = pos ^ swz_x<BK>(r);
-            xoff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * a.K + 8 * c) * 2);
+            xoff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * a.K + 8 * c) * 2 +
+                                            (q % 2 == 0 ? 1024 : 0));
         }
 #pragma unroll
         for (int q = 0; q < C::WQ; ++q) {
@@ -200,11 +209,13 @@ void tile_kernel(TileArgs a) {
             if constexpr (WT) {   // W^T rows n, swizzled like X
                 const int r = idx / C::CPR, pos = idx % C::CPR;
                 const int c = pos ^ swz_x<BK>(r);
-                woff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, cols - 1)) * a.K + 8 * c) * 2);
+                woff[q] = static_cast<uint32_t>(
+                    (static_cast<int64_t>(min(r, cols - 1)) * a.K + 8 * c) * 2 + (q % 2 == 0 ? 1024 : 0));
             } else {
                 const int k = idx / (BN / 8), pos = idx % (BN / 8);
                 const int c = pos ^ swz_w(k);
-                woff[q] = static_cast<uint32_t>((static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2);
+                woff[q] = static_cast<uint32_t>(
+                    (static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2 + (q % 2 == 0 ? 1024 : 0));
             }
         }
         const int nsteps = (p_hi - p_lo) * sps;
@@ -215,17 +226,17 @@ void tile_kernel(TileArgs a) {
             WT ? a.W + static_cast<int64_t>(n0) * a.K + k_first : a.W + k_first * a.N + n0));
         const int64_t wstep = WT ? BK : static_cast<int64_t>(BK) * a.N;   // per K step
 
-        // copy i (0 .. DMA-1) of K step st into its stages: X copies first, then W
-        auto copy = [&](int st, int i) {
+        // copies i and i+1 (i even; XQ and WQ are even, so a pair never mixes X and W)
+        auto copy2 = [&](int st, int i) {
             if (i < C::XQ) {
                 const uint32_t xd = lds_addr(xs_base + (st % C::XSTAGES) * C::XS +
-                                             (C::XQ * uwave + i) * 512);
-                dma16(xbase + static_cast<int64_t>(st) * BK, xoff[i], xd);
+                                             (C::XQ * uwave + i + 1) * 512);
+                dma16x2(xbase + static_cast<int64_t>(st) * BK, xoff[i], xoff[i + 1], xd);
             } else {
                 const int q = i - C::XQ;
                 const uint32_t wd = lds_addr(ws_base + (st % C::WSTAGES) * C::WS +
-                                             (C::WQ * uwave + q) * 512);
-                dma16(wbase + st * wstep, woff[q], wd);
+                                             (C::WQ * uwave + q + 1) * 512);
+                dma16x2(wbase + st * wstep, woff[q], woff[q + 1], wd);
             }
         };
 
@@ -279,7 +290,7 @@ void tile_kernel(TileArgs a) {
 #pragma unroll
         for (int d = 0; d < C::LEAD; ++d)
 #pragma unroll
-            for (int i = 0; i < C::DMA; ++i) copy(min(d, last), i);
+            for (int i = 0; i < C::DMA; i += 2) copy2(min(d, last), i);
         handshake();
 
         // fragments are double-buffered: k step s of any K step uses buffer s % 2 (KS is
@@ -312,7 +323,8 @@ void tile_kernel(TileArgs a) {
                         const int upto = c0 + ((nb * MB + mb + 1) * (c1 - c0) + 7) / 8;
                         while (c < upto) {
                             __builtin_amdgcn_sched_barrier(0);
-                            copy(st2, c++);
+                            copy2(st2, c);
+                            c += 2;
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
