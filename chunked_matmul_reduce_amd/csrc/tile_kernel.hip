@@ -224,19 +224,28 @@ void tile_kernel(TileArgs a) {
             uniform_ptr(a.X + static_cast<int64_t>(m0) * a.K + k_first));
         const uint16_t* wbase = static_cast<const uint16_t*>(uniform_ptr(
             WT ? a.W + static_cast<int64_t>(n0) * a.K + k_first : a.W + k_first * a.N + n0));
-        const int64_t wstep = WT ? BK : static_cast<int64_t>(BK) * a.N;   // per K step
+        // bytes per K step; a step's byte offset st * step fits 32 bits (X, W < 2^31 elements)
+        const uint32_t xstep_b = BK * 2;
+        const uint32_t wstep_b = WT ? BK * 2 : static_cast<uint32_t>(BK * a.N * 2);
+        // stage of K step st (st >= 0: unsigned arithmetic keeps the modulo short)
+        auto xstage = [](int st) { return static_cast<unsigned>(st) % C::XSTAGES; };
+        auto wstage = [](int st) { return static_cast<unsigned>(st) % C::WSTAGES; };
+        auto step_ptr = [](const uint16_t* base, int st, uint32_t step_b) {
+            return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) +
+                                                     static_cast<uint32_t>(st) * step_b);
+        };
 
         // copies i and i+1 (i even; XQ and WQ are even, so a pair never mixes X and W)
         auto copy2 = [&](int st, int i) {
             if (i < C::XQ) {
-                const uint32_t xd = lds_addr(xs_base + (st % C::XSTAGES) * C::XS +
+                const uint32_t xd = lds_addr(xs_base + xstage(st) * C::XS +
                                              (C::XQ * uwave + i + 1) * 512);
-                dma16x2(xbase + static_cast<int64_t>(st) * BK, xoff[i], xoff[i + 1], xd);
+                dma16x2(step_ptr(xbase, st, xstep_b), xoff[i], xoff[i + 1], xd);
             } else {
                 const int q = i - C::XQ;
-                const uint32_t wd = lds_addr(ws_base + (st % C::WSTAGES) * C::WS +
+                const uint32_t wd = lds_addr(ws_base + wstage(st) * C::WS +
                                              (C::WQ * uwave + q + 1) * 512);
-                dma16x2(wbase + st * wstep, woff[q], woff[q + 1], wd);
+                dma16x2(step_ptr(wbase, st, wstep_b), woff[q], woff[q + 1], wd);
             }
         };
 
@@ -252,8 +261,8 @@ void tile_kernel(TileArgs a) {
         const int last = nsteps - 1;
         // operand fragments of MFMA k step s of K step t
         auto frags = [&](int t, int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
-            const uint16_t* xs = xs_base + (t % C::XSTAGES) * C::XS;
-            const uint16_t* wsb = ws_base + (t % C::WSTAGES) * C::WS;
+            const uint16_t* xs = xs_base + xstage(t) * C::XS;
+            const uint16_t* wsb = ws_base + wstage(t) * C::WS;
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int m = C::RW * wm + 32 * mb + l32;
