@@ -92,6 +92,11 @@ RAGGED = [
     (1056, 2048, 544, 8),
     (32, 4096, 4096, 2),
     (64, 131072, 64, 4096),   # the largest P: 4096 slices of K/P = 32
+    # the smallest K and N (copies are issued in pairs whose first copy's source offset
+    # carries +1024 against the instruction's -1024: these keep every offset small)
+    (32, 32, 32, 1),
+    (256, 32, 64, 1),
+    (256, 512, 32, 2),
 ]
 
 
