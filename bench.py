@@ -15,6 +15,7 @@ and the oracle's CPU throughput on a bounded sample of the same workload.  Compa
 legs: the sequential schedule (same kernels, no overlap), the two-stream schedule, and
 the unfused path (one kernel per operation, mask materialized); their ratios to the
 fused time are the one-GPU analogues of the pages' block-level speedups.  Also timed:
+the balanced schedule, the block with a bf16 output,
 the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16; the same flop
 count), the whole MLP (producer then block), the QKV projection in front of the GPT-2
 attention block (bias, no activation), and the data-parallel side (gradient
