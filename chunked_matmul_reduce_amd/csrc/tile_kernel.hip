@@ -43,6 +43,7 @@
 //
 // No fused multiply-add anywhere in the epilogue (built with -ffp-contract=off and
 // written with explicit round-to-nearest add / multiply).
+#include <atomic>
 #include <type_traits>
 
 #include "device_common.h"
@@ -485,13 +486,17 @@ void tile_kernel(TileArgs a) {
 template <int MODE, int BK, bool WT>
 static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
     constexpr int lds = TileCfg<BK>::LDS_BYTES;
-    static bool attr_set = false;
-    if (!attr_set) {
+    // the dynamic-LDS limit is raised once per device (bit d of the mask: device d)
+    static std::atomic<uint64_t> attr_set{0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
+    const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
+    if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
         void (*fn)(TileArgs) = tile_kernel<MODE, BK, WT>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        attr_set = true;
+        attr_set.fetch_or(bit, std::memory_order_release);
     }
     hipLaunchKernelGGL((tile_kernel<MODE, BK, WT>), dim3(grid), dim3(kThreads), lds, s, a);
     return hipGetLastError();
