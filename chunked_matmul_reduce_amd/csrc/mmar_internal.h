@@ -76,9 +76,8 @@ struct AdamArgs {
     float inv_p, lr, b1, b2, one_minus_b1, one_minus_b2, eps, wd, c1, c2;
 };
 
-constexpr int kBM = 256;   // output rows per tile (4 waves x 64)
+constexpr int kBM = 256;   // output rows per tile
 constexpr int kBN = 128;   // output columns per tile
-constexpr int kThreads = 256;
 
 // Launchers (tile_kernel.hip, reduce_kernels.hip).  bk is 64 or 32 (the K step; it must divide Ks).  wt: a.W
 // holds W^T [N, K] instead of W [K, N].

@@ -5,9 +5,12 @@
 // into the collective) folded onto one GPU: P K-slices stand in for P ranks, and a
 // fixed-order fp32 sum of the slice partials stands in for the AllReduce.
 //
-// A 256-thread workgroup (4 waves, one per SIMD) owns a 256 x 128 output tile; wave w
-// owns rows [64w, 64w+64) and all 128 columns, as 2 x 4 blocks of 32 x 32 computed with
-// v_mfma_f32_32x32x16_bf16.  The MFMA computes the transposed block (W^T in the A slot,
+// A workgroup owns a 256 x 128 output tile, computed with v_mfma_f32_32x32x16_bf16 in
+// 32 x 32 blocks.  With 64-deep K steps it has 8 waves, two per SIMD: wave w owns rows
+// [64 (w % 4), +64) and columns [64 (w / 4), +64), as 2 x 2 blocks; the two waves of a
+// SIMD take turns issuing, so one wave's operand reads, copies and waits run while the
+// other's MFMAs execute.  With 32-deep K steps (slices that are not a multiple of 64) it
+// has 4 waves, one per SIMD, each owning 64 rows and all 128 columns as 2 x 4 blocks.  The MFMA computes the transposed block (W^T in the A slot,
 // X in the B slot), so that a lane's accumulator holds one output row and, per group of
 // four registers, four consecutive columns: exactly one Philox group, one 8-byte bias /
 // residual load and one 16-byte fp32 store, with no cross-lane exchange.
@@ -58,15 +61,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define MMAR_LDS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-#ifndef MMAR_WAVES_M
-#define MMAR_WAVES_M 4
-#endif
-
 template <int BK>
 struct TileCfg {
     static constexpr int BM = kBM, BN = kBN;
-    static constexpr int WM = MMAR_WAVES_M;             // waves along m
-    static constexpr int WN = 4 / WM;                   // waves along n
+    // waves per workgroup: 8 (two per SIMD) at BK = 64; at BK = 32 a W stage has too few
+    // 16-byte chunks for 8 waves to copy them in pairs, so 4 (one per SIMD)
+    static constexpr int NW = BK == 64 ? 8 : 4;
+    static constexpr int THREADS = 64 * NW;
+    static constexpr int WM = 4;                        // waves along m
+    static constexpr int WN = NW / WM;                  // waves along n
     static constexpr int RW = BM / WM, CW = BN / WN;    // rows / columns of a wave
     static constexpr int MB = RW / 32, NB = CW / 32;    // 32 x 32 MFMA blocks of a wave
     static constexpr int KS = BK / 16;                  // MFMA k steps per K step
@@ -76,12 +79,12 @@ struct TileCfg {
     static constexpr int XS = BM * BK;                  // elements of an X stage [BM][BK]
     static constexpr int WS = BK * BN;                  // elements of a W stage [BK][BN]
     static constexpr int CPR = BK / 8;                  // 16-byte chunks per X row
-    static constexpr int XQ = XS / 8 / 64 / 4;          // X copy instructions per wave
-    static constexpr int WQ = WS / 8 / 64 / 4;          // W copy instructions per wave
+    static constexpr int XQ = XS / 8 / 64 / NW;         // X copy instructions per wave
+    static constexpr int WQ = WS / 8 / 64 / NW;         // W copy instructions per wave
     static constexpr int DMA = XQ + WQ;                 // copy instructions per wave per step
     static constexpr int LDS_BYTES = (XSTAGES * XS + WSTAGES * WS) * 2;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
-    static_assert(MB * NB == 8, "8 MFMA blocks per wave");
+    static_assert(MB * NB * NW == 32, "32 MFMA blocks per tile");
     static_assert(XQ % 2 == 0 && WQ % 2 == 0, "copies go in pairs");
 };
 
@@ -103,8 +106,8 @@ __device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
 // of X, W or W^T, each under 2^31 elements, stays far below 2^32 - 1024).  M0 is saved and
 // restored.  Inline asm, so that the compiler does not turn
 // the LDS writes into a wait on every later LDS read; the kernel waits on the
-// vector-memory counter itself.  One M0 setting per pair instead of per copy takes 30 of
-// the about 230 instructions a wave issues per 64-deep K step.
+// vector-memory counter itself.  One M0 setting per pair instead of per copy saved about
+// an eighth of the instructions a wave issues per K step.
 __device__ __forceinline__ void dma16x2(const void* sbase, uint32_t voff0, uint32_t voff1,
                                         uint32_t lds_addr1) {
     uint32_t saved;
@@ -140,7 +143,8 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // transpose read; WT = true: W is given transposed, [N, K] (k contiguous, the layout of
 // a Linear layer's weight), and both operands use plain 16-byte LDS reads.
 template <int MODE, int BK, bool WT>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(TileCfg<BK>::THREADS)
+__attribute__((amdgpu_waves_per_eu(TileCfg<BK>::NW / 4, TileCfg<BK>::NW / 4)))
 void tile_kernel(TileArgs a) {
     using C = TileCfg<BK>;
     constexpr int BM = C::BM, BN = C::BN, NB = C::NB, MB = C::MB, KS = C::KS;
@@ -309,7 +313,7 @@ void tile_kernel(TileArgs a) {
         frags(0, 0, xa, wa);
 
         int st = 0;
-        // One K step (step st): KS k steps of 8 MFMAs, the copies of step st+LEAD between
+        // One K step (step st): KS k steps of NB x MB MFMAs, the copies of step st+LEAD between
         // them, the step-boundary handshake before the last k step.  ZERO marks the first
         // K step of a slice: its first k step gives the MFMAs a zero accumulator input,
         // which starts the slice sums from zero without clearing any register.
@@ -318,7 +322,7 @@ void tile_kernel(TileArgs a) {
             // copies of step st+LEAD (the last steps re-copy the last one: identical bytes,
             // no branch), spread over the MFMAs of k steps 0 .. KS-2
             const int st2 = min(st + C::LEAD, last);
-            // the 8 MFMAs of one k step, with copies c0 .. c1-1 issued between them (all of
+            // the NB x MB MFMAs of one k step, with copies c0 .. c1-1 issued between them (all of
             // them: the caller passes c1 - c0 <= DMA)
             auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1,
                              bool zero) {
@@ -329,8 +333,9 @@ void tile_kernel(TileArgs a) {
                     for (int mb = 0; mb < MB; ++mb) {
                         S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                             wf[nb], xf[mb], zero ? f32x16{} : S[nb][mb], 0, 0, 0);
-                        // spread the copies evenly over the 8 MFMAs
-                        const int upto = c0 + ((nb * MB + mb + 1) * (c1 - c0) + 7) / 8;
+                        // spread the copies evenly over the NB x MB MFMAs
+                        const int upto =
+                            c0 + ((nb * MB + mb + 1) * (c1 - c0) + NB * MB - 1) / (NB * MB);
                         while (c < upto) {
                             __builtin_amdgcn_sched_barrier(0);
                             copy2(st2, c);
@@ -498,7 +503,7 @@ static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((tile_kernel<MODE, BK, WT>), dim3(grid), dim3(kThreads), lds, s, a);
+    hipLaunchKernelGGL((tile_kernel<MODE, BK, WT>), dim3(grid), dim3(TileCfg<BK>::THREADS), lds, s, a);
     return hipGetLastError();
 }
 
@@ -525,7 +530,7 @@ static int occ_t() {
     int n = 0;
     const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK, false>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, fn, kThreads,
+            &n, fn, TileCfg<BK>::THREADS,
             static_cast<size_t>(TileCfg<BK>::LDS_BYTES)) != hipSuccess)
         return 0;
     return n;
