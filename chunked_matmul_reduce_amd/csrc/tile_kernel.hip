@@ -9,8 +9,9 @@
 // 32 x 32 blocks.  With 64-deep K steps it has 8 waves, two per SIMD: wave w owns rows
 // [64 (w % 4), +64) and columns [64 (w / 4), +64), as 2 x 2 blocks; the two waves of a
 // SIMD take turns issuing, so one wave's operand reads, copies and waits run while the
-// other's MFMAs execute.  With 32-deep K steps (slices that are not a multiple of 64) it
-// has 4 waves, one per SIMD, each owning 64 rows and all 128 columns as 2 x 4 blocks.  The MFMA computes the transposed block (W^T in the A slot,
+// other's MFMAs execute.  The partials mode, and 32-deep K steps (slices that are not a
+// multiple of 64), use 4 waves, one per SIMD, each owning 64 rows and all 128 columns as
+// 2 x 4 blocks.  The MFMA computes the transposed block (W^T in the A slot,
 // X in the B slot), so that a lane's accumulator holds one output row and, per group of
 // four registers, four consecutive columns: exactly one Philox group, one 8-byte bias /
 // residual load and one 16-byte fp32 store, with no cross-lane exchange.
@@ -61,12 +62,19 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define MMAR_LDS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-template <int BK>
+// Waves per workgroup: 8 (two per SIMD) for the modes that keep a tile's result in
+// registers over all its K steps (the fused block 5-6 % faster, the producer MatMul 2-4 %
+// faster than with 4 waves); 4 (one per SIMD) for the partials mode, whose work items are
+// one slice long (12 % slower with 8 waves), and at BK = 32, where a W stage has too few
+// 16-byte chunks for 8 waves to copy them in pairs.
+constexpr int tile_waves(int mode, int bk) {
+    return bk != 64 || mode == kModePartials ? 4 : 8;
+}
+
+template <int BK, int NW_>
 struct TileCfg {
     static constexpr int BM = kBM, BN = kBN;
-    // waves per workgroup: 8 (two per SIMD) at BK = 64; at BK = 32 a W stage has too few
-    // 16-byte chunks for 8 waves to copy them in pairs, so 4 (one per SIMD)
-    static constexpr int NW = BK == 64 ? 8 : 4;
+    static constexpr int NW = NW_;
     static constexpr int THREADS = 64 * NW;
     static constexpr int WM = 4;                        // waves along m
     static constexpr int WN = NW / WM;                  // waves along n
@@ -143,10 +151,10 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // transpose read; WT = true: W is given transposed, [N, K] (k contiguous, the layout of
 // a Linear layer's weight), and both operands use plain 16-byte LDS reads.
 template <int MODE, int BK, bool WT>
-__global__ __launch_bounds__(TileCfg<BK>::THREADS)
-__attribute__((amdgpu_waves_per_eu(TileCfg<BK>::NW / 4, TileCfg<BK>::NW / 4)))
+__global__ __launch_bounds__(64 * tile_waves(MODE, BK))
+__attribute__((amdgpu_waves_per_eu(tile_waves(MODE, BK) / 4, tile_waves(MODE, BK) / 4)))
 void tile_kernel(TileArgs a) {
-    using C = TileCfg<BK>;
+    using C = TileCfg<BK, tile_waves(MODE, BK)>;
     constexpr int BM = C::BM, BN = C::BN, NB = C::NB, MB = C::MB, KS = C::KS;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* const xs_base = smem;                       // [XSTAGES][BM][BK], swizzled
@@ -490,7 +498,8 @@ void tile_kernel(TileArgs a) {
 // ------------------------------------------------------------------ launchers
 template <int MODE, int BK, bool WT>
 static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
-    constexpr int lds = TileCfg<BK>::LDS_BYTES;
+    using C = TileCfg<BK, tile_waves(MODE, BK)>;
+    constexpr int lds = C::LDS_BYTES;
     // the dynamic-LDS limit is raised once per device (bit d of the mask: device d)
     static std::atomic<uint64_t> attr_set{0};
     int dev = 0;
@@ -503,7 +512,7 @@ static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((tile_kernel<MODE, BK, WT>), dim3(grid), dim3(TileCfg<BK>::THREADS), lds, s, a);
+    hipLaunchKernelGGL((tile_kernel<MODE, BK, WT>), dim3(grid), dim3(C::THREADS), lds, s, a);
     return hipGetLastError();
 }
 
@@ -530,8 +539,8 @@ static int occ_t() {
     int n = 0;
     const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK, false>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, fn, TileCfg<BK>::THREADS,
-            static_cast<size_t>(TileCfg<BK>::LDS_BYTES)) != hipSuccess)
+            &n, fn, TileCfg<BK, tile_waves(MODE, BK)>::THREADS,
+            static_cast<size_t>(TileCfg<BK, tile_waves(MODE, BK)>::LDS_BYTES)) != hipSuccess)
         return 0;
     return n;
 }
