@@ -83,7 +83,9 @@ struct TileCfg {
     static constexpr int KS = BK / 16;                  // MFMA k steps per K step
     static constexpr int LEAD = BK == 64 ? 2 : 5;       // copies run LEAD K steps ahead
     static constexpr int XSTAGES = LEAD + 1;            // X ring depth
-    static constexpr int WSTAGES = LEAD + 2;            // W ring depth (one more: early barrier)
+    static constexpr int WSTAGES = LEAD + 2;            // W ring depth (one more than X:
+                                                        // W copies never reuse the stage
+                                                        // of the step just read)
     static constexpr int XS = BM * BK;                  // elements of an X stage [BM][BK]
     static constexpr int WS = BK * BN;                  // elements of a W stage [BK][BN]
     static constexpr int CPR = BK / 8;                  // 16-byte chunks per X row
@@ -105,6 +107,8 @@ __device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding).
 #define MMAR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
+// The same, and every LDS read of this wave complete (lgkmcnt 0).
+#define MMAR_WAIT_VM_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | ((((n) >> 4) & 3) << 14))
 
 // Two 16-byte global -> LDS copies per lane with one M0 setting (sbase wave-uniform in
 // SGPRs, voff0 / voff1 per-lane byte offsets, lds_addr1 wave-uniform): copy 0 reads
@@ -302,10 +306,12 @@ void tile_kernel(TileArgs a) {
         };
         // Step-boundary handshake for K step t: this wave's copies of t are done (only the
         // copies of the LEAD - 1 following steps may remain) and the barrier makes every
-        // wave's copies of t visible; it also shows that every wave finished step t-2, whose
-        // W stage the copies issued next (for step t + LEAD) reuse.
+        // wave's copies of t visible.  Each wave also waits for its own LDS reads (the
+        // operands of step t-1's last k step, read just before), so the barrier shows that
+        // every wave has finished reading step t-1, whose X stage the copies issued next
+        // (for step t + LEAD) overwrite, and step t-2, whose W stage they overwrite.
         auto handshake = [&]() {
-            MMAR_WAIT_VM((C::LEAD - 1) * C::DMA);
+            MMAR_WAIT_VM_LDS((C::LEAD - 1) * C::DMA);
             wg_barrier();
         };
 
@@ -384,8 +390,9 @@ void tile_kernel(TileArgs a) {
                   for (int mb = 0; mb < MB; ++mb) T[nb][mb] += S[nb][mb];
           }
         }
-        MMAR_WAIT_VM(0);
-        wg_barrier();   // every wave is done with the LDS ring before the next item's copies
+        MMAR_WAIT_VM_LDS(0);
+        wg_barrier();   // every wave is done with the LDS ring (its copies landed, its reads
+                        // returned) before the next item's copies
 
         // Store / epilogue.  Lane holds rows RW wm + 32 mb + l32 and, in registers
         // 4g..4g+3 of block nb, columns CW wn + 32 nb + 8 g + 4 h + 0..3.  A ragged tile
