@@ -245,9 +245,11 @@ std::pair<int, int> balanced_split(const Shape& s, int g) {
 }
 
 // The default plan is the persistent schedule.  The balanced schedule is left to the
-// autotuner: on the BERT-shaped block (640 tiles: two full rounds and a half one) it ran
-// as fast as the persistent schedule, whose half-empty last round runs faster than a
-// full one, not half a round faster.
+// autotuner: where the last round of tiles is partial it won on some shapes (the
+// BERT-shaped block, 640 tiles with P = 8: 3 % faster) and lost on others (P = 16 tails,
+// whose 16 one-slice partials per tile cost more than the idle part of the round: 8-10 %
+// slower), and the persistent schedule's half-empty last round runs faster than a full
+// one, not half a round faster.
 Plan default_plan(const Shape& s, int) {
     Plan p;
     p.sched = MMAR_SCHED_PERSISTENT;
