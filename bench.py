@@ -26,6 +26,8 @@ The default warm-up (50 steps, about 30 ms) takes the GPU past the clock transie
 its first launches; the timed steps then run at the sustained clock.
 
 --only fused     time only the fused block (for rocprofv3 runs)
+--only streams   time only the two-stream schedule (for a kernel-trace timeline of its
+                 chunk pipeline)
 --only copy      one plain 1 GiB device copy, the calibration point for HBM counters
 """
 import argparse
@@ -123,13 +125,13 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gpt2_mlp")
-    ap.add_argument("--only", choices=["all", "fused", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "fused", "streams", "copy"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(the P ranks are folded onto one device as K-slices)", file=sys.stderr)
         sys.exit(2)
 
@@ -162,6 +164,18 @@ def main():
 
     def fused():
         mmar.fused(X, W, bias, res, P, p, seed, out=out)
+
+    if args.only == "streams":
+        def streams():
+            mmar.fused_ex(X, W, bias, res, P, p, seed, "streams", out=out)
+        for _ in range(args.warmup):
+            streams()
+        torch.cuda.synchronize()
+        med, mean = _ev_time(torch, streams, args.steps)
+        print(json.dumps({"schedule": "streams", "workload": w.name, "steps": args.steps,
+                          "median_us": round(med * 1e3, 2), "mean_us": round(mean * 1e3, 2)}),
+              flush=True)
+        return
 
     for _ in range(args.warmup):
         fused()
