@@ -450,8 +450,8 @@ int grid_for(const DevState* st, int mode, int bk, int items) {
     return std::max(1, std::min(items, resident));
 }
 
-int tiles_in(int rows, int cols) {
-    return ((rows + mmar::kBM - 1) / mmar::kBM) * ((cols + mmar::kBN - 1) / mmar::kBN);
+int tiles_in(int rows, int cols, int bn = mmar::kBN) {
+    return ((rows + mmar::kBM - 1) / mmar::kBM) * ((cols + bn - 1) / bn);
 }
 
 TileArgs tile_args(const Call& c, int rm0, int rn0, int RM, int RN, int cm, int cn) {
@@ -483,7 +483,7 @@ int run_persistent(const DevState* st, const Call& c, int mode, int cm, int cn, 
     const int bk = bk_for(c.s);
     TileArgs a = tile_args(c, 0, 0, static_cast<int>(c.s.M), static_cast<int>(c.s.N), cm, cn);
     const int64_t items =
-        static_cast<int64_t>(c.s.M / cm) * (c.s.N / cn) * tiles_in(cm, cn);
+        static_cast<int64_t>(c.s.M / cm) * (c.s.N / cn) * tiles_in(cm, cn, mmar::tile_bn(mode));
     a.total_items = static_cast<int32_t>(items);
     MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, a, grid_for(st, mode, bk, a.total_items), s));
     return MMAR_OK;
@@ -947,6 +947,26 @@ int mmar_adam_step(const float* grads, float* param, float* m, float* v, uint16_
     return MMAR_OK;
 }
 
+// Tile of the producer MatMul: 256 x 256 (a third fewer copied bytes and a quarter fewer
+// LDS operand reads per flop than 256 x 128) unless its tile count fills the last round
+// of the CUs worse than the 128-wide tiles do.  MMAR_LINEAR_TILE=128 or 256 forces one
+// (for measurements).
+static int linear_mode(const DevState* st, int64_t M, int64_t N) {
+    const char* e = std::getenv("MMAR_LINEAR_TILE");
+    const int forced = e ? std::atoi(e) : 0;
+    if (forced == 128) return mmar::kModeLinear;
+    if (forced == 256) return mmar::kModeLinearWide;
+    if (N < mmar::kBNWide) return mmar::kModeLinear;
+    const int cus = std::max(1, st->cus);
+    auto fill = [cus](int64_t tiles) {
+        const int64_t rounds = (tiles + cus - 1) / cus;
+        return static_cast<double>(tiles) / static_cast<double>(rounds * cus);
+    };
+    const double wide = fill(tiles_in(static_cast<int>(M), static_cast<int>(N), mmar::kBNWide));
+    const double narrow = fill(tiles_in(static_cast<int>(M), static_cast<int>(N)));
+    return wide >= narrow ? mmar::kModeLinearWide : mmar::kModeLinear;
+}
+
 int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
                 int64_t M, int64_t N, int64_t K, int32_t activation, void* stream) {
     g_err.clear();
@@ -973,7 +993,7 @@ int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint
     c.act = activation == MMAR_ACT_GELU_TANH ? mmar::kActGeluTanh : mmar::kActNone;
     c.s = s;
     c.w_t = false;
-    return run_persistent(st, c, mmar::kModeLinear, static_cast<int>(M), static_cast<int>(N),
+    return run_persistent(st, c, linear_mode(st, M, N), static_cast<int>(M), static_cast<int>(N),
                           static_cast<hipStream_t>(stream));
 }
 

@@ -15,8 +15,10 @@ enum TileMode : int {
     kModePartials = 2,  // one slice per work item, stored as fp32 S_p to a workspace
     kModeLinear = 3,    // all slices (the producer MatMul has P = 1), + bias, activation,
                         // bf16 out
+    kModeLinearWide = 4,  // kModeLinear for one slice on 256 x 256 tiles (no running total,
+                          // so the registers hold a tile twice as wide)
 };
-constexpr int kNumModes = 4;
+constexpr int kNumModes = 5;
 
 // Activation of kModeLinear (the values of the public MMAR_ACT_* constants).
 enum Activation : int {
@@ -78,9 +80,11 @@ struct AdamArgs {
 
 constexpr int kBM = 256;   // output rows per tile
 constexpr int kBN = 128;   // output columns per tile
+constexpr int kBNWide = 256;   // output columns per tile of kModeLinearWide
+constexpr int tile_bn(int mode) { return mode == kModeLinearWide ? kBNWide : kBN; }
 
-// Launchers (tile_kernel.hip, reduce_kernels.hip).  bk is 64 or 32 (the K step; it must divide Ks).  wt: a.W
-// holds W^T [N, K] instead of W [K, N].
+// Launchers (tile_kernel.hip, reduce_kernels.hip).  bk is 64 or 32 (the K step; it must divide Ks;
+// kModeLinearWide always steps by 32).  wt: a.W holds W^T [N, K] instead of W [K, N].
 hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, hipStream_t s);
 hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, hipStream_t s);
 hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s);

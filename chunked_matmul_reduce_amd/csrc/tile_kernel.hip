@@ -68,12 +68,16 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // one slice long (12 % slower with 8 waves), and at BK = 32, where a W stage has too few
 // 16-byte chunks for 8 waves to copy them in pairs.
 constexpr int tile_waves(int mode, int bk) {
-    return bk != 64 || mode == kModePartials ? 4 : 8;
+    return mode == kModeLinearWide ? 8 : bk != 64 || mode == kModePartials ? 4 : 8;
 }
+// K step of a mode's kernel: the wide producer tile always steps by 32 (two 64-deep
+// stages of a 256 x 256 tile would not fit the LDS with copies two steps ahead).
+constexpr int tile_bk(int mode, int bk) { return mode == kModeLinearWide ? 32 : bk; }
+constexpr bool is_linear(int mode) { return mode == kModeLinear || mode == kModeLinearWide; }
 
-template <int BK, int NW_>
+template <int BK, int NW_, int BN_ = kBN>
 struct TileCfg {
-    static constexpr int BM = kBM, BN = kBN;
+    static constexpr int BM = kBM, BN = BN_;
     static constexpr int NW = NW_;
     static constexpr int THREADS = 64 * NW;
     static constexpr int WM = 4;                        // waves along m
@@ -81,7 +85,8 @@ struct TileCfg {
     static constexpr int RW = BM / WM, CW = BN / WN;    // rows / columns of a wave
     static constexpr int MB = RW / 32, NB = CW / 32;    // 32 x 32 MFMA blocks of a wave
     static constexpr int KS = BK / 16;                  // MFMA k steps per K step
-    static constexpr int LEAD = BK == 64 ? 2 : 5;       // copies run LEAD K steps ahead
+    static constexpr int LEAD = BK == 64 ? 2 : BN == 256 ? 3 : 5;   // copies run LEAD K
+                                                                    // steps ahead
     static constexpr int XSTAGES = LEAD + 1;            // X ring depth
     static constexpr int WSTAGES = LEAD + 2;            // W ring depth (one more than X:
                                                         // W copies never reuse the stage
@@ -94,7 +99,7 @@ struct TileCfg {
     static constexpr int DMA = XQ + WQ;                 // copy instructions per wave per step
     static constexpr int LDS_BYTES = (XSTAGES * XS + WSTAGES * WS) * 2;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
-    static_assert(MB * NB * NW == 32, "32 MFMA blocks per tile");
+    static_assert(MB * NB * NW * 1024 == BM * BN, "the waves' 32 x 32 blocks cover the tile");
     static_assert(XQ % 2 == 0 && WQ % 2 == 0, "copies go in pairs");
 };
 
@@ -158,7 +163,9 @@ template <int MODE, int BK, bool WT>
 __global__ __launch_bounds__(64 * tile_waves(MODE, BK))
 __attribute__((amdgpu_waves_per_eu(tile_waves(MODE, BK) / 4, tile_waves(MODE, BK) / 4)))
 void tile_kernel(TileArgs a) {
-    using C = TileCfg<BK, tile_waves(MODE, BK)>;
+    using C = TileCfg<BK, tile_waves(MODE, BK), tile_bn(MODE)>;
+    // one slice and no running total: the wide producer tile stores S itself
+    constexpr bool NO_T = MODE == kModeLinearWide || MODE == kModePartials;
     constexpr int BM = C::BM, BN = C::BN, NB = C::NB, MB = C::MB, KS = C::KS;
     extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
     uint16_t* const xs_base = smem;                       // [XSTAGES][BM][BK], swizzled
@@ -381,7 +388,7 @@ void tile_kernel(TileArgs a) {
           kstep(std::true_type{});
           ++st;
           for (int j = 1; j < sps; ++j, ++st) kstep(std::false_type{});
-          if (MODE != kModePartials) {
+          if constexpr (!NO_T) {
               // T = 0 + S_0 (= S_0 exactly: an MFMA sum started from +0 is never -0),
               // then T + S_1, T + S_2, ... in fp32, round to nearest even
 #pragma unroll
@@ -402,7 +409,7 @@ void tile_kernel(TileArgs a) {
         // arithmetic) instead of one load latency per output group.
         auto col_ok = [&](int nb) { return C::CW * wn + 32 * nb < cols; };
         auto row_ok = [&](int mb) { return C::RW * wm + 32 * mb < rows; };
-        if constexpr (MODE == kModeLinear) {
+        if constexpr (is_linear(MODE)) {
             uint2 bb[NB][4];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -422,7 +429,9 @@ void tile_kernel(TileArgs a) {
                             if (!col_ok(nb) || !row_ok(mb)) continue;
                             const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
                             const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
-                            const f32x16& acc = T[nb][mb];
+                            // the wide tile has one slice: S, as it comes from the MFMAs
+                            // (a sum started from +0, never -0), equals T = 0 + S
+                            const f32x16& acc = NO_T ? S[nb][mb] : T[nb][mb];
                             const uint2 b = bb[nb][g];
                             const float g0 = act(__fadd_rn(acc[4 * g], bf16_lo(b.x)));
                             const float g1 = act(__fadd_rn(acc[4 * g + 1], bf16_hi(b.x)));
@@ -505,7 +514,7 @@ void tile_kernel(TileArgs a) {
 // ------------------------------------------------------------------ launchers
 template <int MODE, int BK, bool WT>
 static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
-    using C = TileCfg<BK, tile_waves(MODE, BK)>;
+    using C = TileCfg<BK, tile_waves(MODE, BK), tile_bn(MODE)>;
     constexpr int lds = C::LDS_BYTES;
     // the dynamic-LDS limit is raised once per device (bit d of the mask: device d)
     static std::atomic<uint64_t> attr_set{0};
@@ -525,6 +534,7 @@ static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
 
 template <bool WT>
 static hipError_t launch_tile_w(int mode, int bk, const TileArgs& a, int grid, hipStream_t s) {
+    if (mode == kModeLinearWide) return launch_tile_t<kModeLinearWide, 32, WT>(a, grid, s);
     if (bk == 64) {
         if (mode == kModeFused) return launch_tile_t<kModeFused, 64, WT>(a, grid, s);
         if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64, WT>(a, grid, s);
@@ -543,16 +553,17 @@ hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, h
 
 template <int MODE, int BK>
 static int occ_t() {
+    using C = TileCfg<BK, tile_waves(MODE, BK), tile_bn(MODE)>;
     int n = 0;
     const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK, false>);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, fn, TileCfg<BK, tile_waves(MODE, BK)>::THREADS,
-            static_cast<size_t>(TileCfg<BK, tile_waves(MODE, BK)>::LDS_BYTES)) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, C::THREADS,
+                                                     static_cast<size_t>(C::LDS_BYTES)) != hipSuccess)
         return 0;
     return n;
 }
 
 int tile_occupancy(int mode, int bk) {
+    if (mode == kModeLinearWide) return occ_t<kModeLinearWide, 32>();
     if (bk == 64) {
         if (mode == kModeFused) return occ_t<kModeFused, 64>();
         if (mode == kModeReduced) return occ_t<kModeReduced, 64>();

@@ -141,3 +141,40 @@ def test_linear_rejects_an_unknown_activation():
     mmar.linear(X, W, b, "none", out=H)
     torch.cuda.synchronize()
     assert np.all(host(H.float()) == 1.0)        # 0 + bias
+
+
+# The producer's two tile widths: 256 x 128, and 256 x 256 (one slice needs no running
+# total, so a tile twice as wide fits the registers).  Shapes with ragged row and column
+# tiles, K shorter than the copies' lead (3 steps of 32), and several tiles.
+WIDE_SHAPES = [(64, 256, 256), (288, 480, 544), (1056, 2048, 544), (32, 4096, 4096),
+               (256, 64, 512), (544, 1024, 2592)]
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "none"])
+@pytest.mark.parametrize("M,K,N", WIDE_SHAPES)
+def test_wide_tile_matches_narrow_bits_and_oracle(M, K, N, act, monkeypatch):
+    print("producer tiles", M, K, N, act, flush=True)
+    inp = make_random_inputs(M, K, N, seed=M * 7 + N + K)
+    X, W, b = (dev(inp[k], torch) for k in ("X", "W", "bias"))
+    monkeypatch.setenv("MMAR_LINEAR_TILE", "256")
+    Hw = mmar.linear(X, W, b, act)
+    monkeypatch.setenv("MMAR_LINEAR_TILE", "128")
+    Hn = mmar.linear(X, W, b, act)
+    torch.cuda.synchronize()
+    assert np.array_equal(_h_bits(Hw), _h_bits(Hn))
+    h, _, bound = producer.producer(inp["X"], inp["W"], inp["bias"], activation=act)
+    ties = producer.check_bf16_output(_h_bits(Hw), h, bound)
+    assert ties < 0.7 * M * N
+
+
+def test_wide_tile_full_size_gelu_layer_bits(monkeypatch):
+    """The GPT-2 MLP block's first layer on both tile widths: identical bits."""
+    w = WORKLOADS["gpt2_mlp"]
+    pin = make_producer_inputs(w)
+    X0, W1, b1 = (dev(pin[k], torch) for k in ("X0", "W1", "b1"))
+    monkeypatch.setenv("MMAR_LINEAR_TILE", "256")
+    Hw = mmar.gelu_linear(X0, W1, b1)
+    monkeypatch.setenv("MMAR_LINEAR_TILE", "128")
+    Hn = mmar.gelu_linear(X0, W1, b1)
+    torch.cuda.synchronize()
+    assert torch.equal(Hw.view(torch.int16), Hn.view(torch.int16))
