@@ -275,6 +275,13 @@ def main():
                           reps)[0]
         del outb
         del parts
+        # one rank's share on its own, at its real shape: the GEMM of one K-slice (P = 1,
+        # K / P deep) with its fp32 output, what each of P tensor-parallel GPUs would run
+        # before the exchange
+        ks = w.K // P
+        Xr, Wr = X[:, :ks].contiguous(), W[:ks].contiguous()
+        t_rank = _ev_time(torch, lambda: mmar.gemm_only(Xr, Wr, 1, out=T), reps)[0]
+        del Xr, Wr, T
         torch.cuda.empty_cache()
         # the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16) and the
         # whole MLP (producer then block), on the producer's seeded inputs
@@ -350,6 +357,11 @@ def main():
         result["speedup_vs_sequential"] = round(t_seq / t_fused, 3)
         result["speedup_streams_vs_sequential"] = round(t_seq / t_str, 3)
         result["speedup_vs_unfused"] = round(t_unf / t_fused, 3)
+        rank_flops = 2.0 * w.M * w.N * (w.K // P)
+        result["per_rank_gemm"] = {"us": round(t_rank * 1e3, 2),
+                                   "TFLOP/s": round(rank_flops / (t_rank * 1e-3) / 1e12, 2),
+                                   "out_GBps": round(4.0 * w.M * w.N / (t_rank * 1e-3) / 1e9, 1),
+                                   "shape": f"[{w.M},{w.K // P}] x [{w.K // P},{w.N}] -> fp32, one slice"}
         result["producer_gelu"] = {"us": round(t_prod * 1e3, 2),
                                    "TFLOP/s": round(flops / (t_prod * 1e-3) / 1e12, 2),
                                    "shape": f"[{w.M},{w.N}] x [{w.N},{w.K}] -> bf16 [{w.M},{w.K}]"}
