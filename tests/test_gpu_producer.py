@@ -178,3 +178,34 @@ def test_wide_tile_full_size_gelu_layer_bits(monkeypatch):
     Hn = mmar.gelu_linear(X0, W1, b1)
     torch.cuda.synchronize()
     assert torch.equal(Hw.view(torch.int16), Hn.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["bert_mlp", "gpt3_mlp"])
+def test_wide_tile_full_size_other_mlp_layers(name, monkeypatch):
+    """The first MLP layers of the BERT- and GPT-3-shaped blocks ([8192, 2560] x [2560,
+    10240] and [2048, 12288] x [12288, 49152]), which the tile choice runs on 256 x 256
+    tiles: bits equal to the 256 x 128 tile on every element, and sampled rows against the
+    oracle.  Inputs drawn on the device with the workloads' distributions (bf16)."""
+    w = WORKLOADS[name]
+    M, K, N = w.M, w.N, w.K            # the producer maps [M, N] to [M, K] of the block
+    print("wide producer", name, M, K, N, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed + 300)
+    X0 = torch.randn((M, K), generator=g, device="cuda").mul_(w.sigma_x).to(torch.bfloat16)
+    W1 = torch.randn((K, N), generator=g, device="cuda").mul_(w.sigma_w).to(torch.bfloat16)
+    b1 = torch.randn((N,), generator=g, device="cuda").mul_(w.sigma_bias).to(torch.bfloat16)
+    monkeypatch.delenv("MMAR_LINEAR_TILE", raising=False)
+    Ha = mmar.gelu_linear(X0, W1, b1)            # the library's own choice
+    monkeypatch.setenv("MMAR_LINEAR_TILE", "256")
+    Hw = mmar.gelu_linear(X0, W1, b1)
+    monkeypatch.setenv("MMAR_LINEAR_TILE", "128")
+    Hn = mmar.gelu_linear(X0, W1, b1)
+    torch.cuda.synchronize()
+    assert torch.equal(Hw.view(torch.int16), Hn.view(torch.int16))
+    assert torch.equal(Ha.view(torch.int16), Hn.view(torch.int16))
+    rows = np.array([0, 1, 255, 256, M // 2, M - 1])
+    xb = host(X0[torch.as_tensor(rows, device="cuda")].view(torch.int16)).view(np.uint16)
+    wb = host(W1.view(torch.int16)).view(np.uint16)
+    bb = host(b1.view(torch.int16)).view(np.uint16)
+    h, _, bound = producer.producer(xb, wb, bb)
+    producer.check_bf16_output(_h_bits(Hw)[rows], h, bound)
