@@ -344,6 +344,43 @@ def test_autotune_keeps_bits():
     assert mmar.get_plan(M, N, K, P)["schedule"] == mmar.SCHED_PERSISTENT
 
 
+@pytest.mark.parametrize("name", ["gpt2_mlp", "gpt2_attn", "bert_mlp", "gpt3_mlp"])
+def test_full_size_tuned_plan(name):
+    """The configuration the benchmark times: the plan mmar_autotune picks for the
+    workload (after warm-up calls, as the benchmark does), bit-identical to the default
+    plan; for the benchmark's own workload, the tuned call on its seeded inputs against
+    the oracle on sampled rows and the dropped elements."""
+    w = WORKLOADS[name]
+    M, K, N, P = w.M, w.K, w.N, w.P
+    print("tuned plan", name, flush=True)
+    if name == "gpt2_mlp":
+        inp = make_inputs(name)
+        d = _to_dev(inp)
+        p, seed = inp["p_drop"], w.seed
+    else:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(w.seed + 400)
+        d = {"X": torch.randn((M, K), generator=g, device="cuda").mul_(w.sigma_x).to(torch.bfloat16),
+             "W": torch.randn((K, N), generator=g, device="cuda").mul_(w.sigma_w).to(torch.bfloat16),
+             "bias": torch.randn((N,), generator=g, device="cuda").mul_(w.sigma_bias).to(torch.bfloat16),
+             "residual": torch.randn((M, N), generator=g, device="cuda").mul_(w.sigma_res).to(torch.bfloat16)}
+        p, seed = np.float32(0.1), w.seed
+    try:
+        ref = f32_bits(_run(d, P, p, seed, "persistent", w_mode="direct"))
+        for _ in range(10):
+            _run(d, P, p, seed)
+        mmar.autotune(M, N, K, P)
+        plan = mmar.get_plan(M, N, K, P)
+        print("tuned", name, plan, flush=True)
+        out = _run(d, P, p, seed)
+        assert np.array_equal(f32_bits(out), ref), plan
+        if name == "gpt2_mlp":
+            rows = _sample_rows(M, np.random.default_rng(w.seed + 1))
+            _check_block(inp, out, rows=rows)
+    finally:
+        mmar.set_plan(M, N, K, P, "auto")
+
+
 # ---------------------------------------------------------------- unfused comparison path
 UNFUSED_CASES = ["tiny", (288, 480, 160, 5), (1056, 2048, 544, 8), "gpt2_attn"]
 
