@@ -947,24 +947,46 @@ int mmar_adam_step(const float* grads, float* param, float* m, float* v, uint16_
     return MMAR_OK;
 }
 
-// Tile of the producer MatMul: 256 x 256 (a third fewer copied bytes and a quarter fewer
-// LDS operand reads per flop than 256 x 128) unless its tile count fills the last round
-// of the CUs worse than the 128-wide tiles do.  MMAR_LINEAR_TILE=128 or 256 forces one
-// (for measurements).
-static int linear_mode(const DevState* st, int64_t M, int64_t N) {
+// Columns of the producer MatMul on 256 x 256 tiles (the rest on 256 x 128).  A 256 x 256
+// tile copies a third fewer bytes and reads a quarter fewer LDS operand bytes per flop;
+// measured on the GPT-2 MLP's first layer it takes 0.91 of the time of two 256 x 128
+// tiles.  With that ratio and whole rounds of the CUs as the cost, the leading columns go
+// to the wide tile in multiples of 256 and the rest to the narrow one, so a tile count that
+// would leave the wide tiles' last round part-empty (the QKV projection: 1152 wide tiles,
+// 4.5 rounds of 256 CUs) is split instead (1024 wide tiles, then 256 narrow ones).  The
+// bits do not depend on the split.  MMAR_LINEAR_TILE = 128 or 256 puts every column on one
+// tile width (for measurements).
+static int64_t linear_wide_columns(const DevState* st, int64_t M, int64_t N) {
     const char* e = std::getenv("MMAR_LINEAR_TILE");
     const int forced = e ? std::atoi(e) : 0;
-    if (forced == 128) return mmar::kModeLinear;
-    if (forced == 256) return mmar::kModeLinearWide;
-    if (N < mmar::kBNWide) return mmar::kModeLinear;
-    const int cus = std::max(1, st->cus);
-    auto fill = [cus](int64_t tiles) {
-        const int64_t rounds = (tiles + cus - 1) / cus;
-        return static_cast<double>(tiles) / static_cast<double>(rounds * cus);
-    };
-    const double wide = fill(tiles_in(static_cast<int>(M), static_cast<int>(N), mmar::kBNWide));
-    const double narrow = fill(tiles_in(static_cast<int>(M), static_cast<int>(N)));
-    return wide >= narrow ? mmar::kModeLinearWide : mmar::kModeLinear;
+    if (forced == 128) return 0;
+    if (forced == 256) return N;
+    const int64_t cus = std::max(1, st->cus);
+    auto rounds = [cus](int64_t tiles) { return (tiles + cus - 1) / cus; };
+    constexpr double kWideRound = 2 * 0.91;   // a round of wide tiles, in narrow rounds
+    int64_t best_nw = 0;
+    double best = static_cast<double>(rounds(tiles_in(static_cast<int>(M), static_cast<int>(N))));
+    for (int64_t nw = mmar::kBNWide; nw <= N; nw += mmar::kBNWide) {
+        const double cost =
+            kWideRound * rounds(tiles_in(static_cast<int>(M), static_cast<int>(nw), mmar::kBNWide)) +
+            (nw < N ? rounds(tiles_in(static_cast<int>(M), static_cast<int>(N - nw))) : 0);
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_nw = nw;
+        }
+    }
+    return best_nw;
+}
+
+// The producer MatMul over output columns [n0, n0 + cols) with one tile width.
+static int run_linear_columns(const DevState* st, const Call& c, int mode, int n0, int cols,
+                              hipStream_t s) {
+    const int bk = bk_for(c.s);
+    const int M = static_cast<int>(c.s.M);
+    TileArgs a = tile_args(c, 0, n0, M, cols, M, cols);
+    a.total_items = static_cast<int32_t>(tiles_in(M, cols, mmar::tile_bn(mode)));
+    MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, a, grid_for(st, mode, bk, a.total_items), s));
+    return MMAR_OK;
 }
 
 int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
@@ -993,8 +1015,14 @@ int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint
     c.act = activation == MMAR_ACT_GELU_TANH ? mmar::kActGeluTanh : mmar::kActNone;
     c.s = s;
     c.w_t = false;
-    return run_persistent(st, c, linear_mode(st, M, N), static_cast<int>(M), static_cast<int>(N),
-                          static_cast<hipStream_t>(stream));
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int64_t nw = linear_wide_columns(st, M, N);
+    if (nw > 0 && (rc = run_linear_columns(st, c, mmar::kModeLinearWide, 0, static_cast<int>(nw), hs)))
+        return rc;
+    if (nw < N)
+        return run_linear_columns(st, c, mmar::kModeLinear, static_cast<int>(nw),
+                                  static_cast<int>(N - nw), hs);
+    return MMAR_OK;
 }
 
 int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,

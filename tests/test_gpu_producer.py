@@ -209,3 +209,29 @@ def test_wide_tile_full_size_other_mlp_layers(name, monkeypatch):
     bb = host(b1.view(torch.int16)).view(np.uint16)
     h, _, bound = producer.producer(xb, wb, bb)
     producer.check_bf16_output(_h_bits(Hw)[rows], h, bound)
+
+
+@pytest.mark.parametrize("M,K,N", [(8192, 3072, 9216), (8192, 3072, 3072), (2080, 512, 1312)])
+def test_column_split_between_tile_widths(M, K, N, monkeypatch):
+    """Shapes whose columns the library splits between 256 x 256 and 256 x 128 tiles (the
+    GPT-2 QKV projection; an attention-shaped layer) or not (a ragged one): the bits of
+    the library's choice equal those of either tile width alone."""
+    print("column split", M, K, N, flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(M + K + N)
+    X = torch.randn((M, K), generator=g, device="cuda").to(torch.bfloat16)
+    W = torch.randn((K, N), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+    b = torch.randn((N,), generator=g, device="cuda").mul_(0.02).to(torch.bfloat16)
+    outs = {}
+    for tile in ("auto", "256", "128"):
+        if tile == "auto":
+            monkeypatch.delenv("MMAR_LINEAR_TILE", raising=False)
+        else:
+            monkeypatch.setenv("MMAR_LINEAR_TILE", tile)
+        for act in ("none", "gelu_tanh"):
+            outs[(tile, act)] = mmar.linear(X, W, b, act)
+    torch.cuda.synchronize()
+    for act in ("none", "gelu_tanh"):
+        ref = outs[("128", act)].view(torch.int16)
+        assert torch.equal(outs[("auto", act)].view(torch.int16), ref), act
+        assert torch.equal(outs[("256", act)].view(torch.int16), ref), act
