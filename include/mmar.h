@@ -196,9 +196,10 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
  * to bf16 (nearest even).  Column block p of H is what rank p of the column-parallel
  * layer would own, and it is exactly K-slice p of the block that follows, so H feeds
  * mmar_fused directly as its X.  Preconditions as mmar_fused with P = 1.  No
- * workspace.  The output tiles are 256 x 256 where their count fills the CUs' last round
- * at least as well as 256 x 128 tiles do, else 256 x 128 (the environment variable
- * MMAR_LINEAR_TILE = 128 or 256 forces one, for measurements); the bits are the same. */
+ * workspace.  The leading output columns (a multiple of 256) are computed on 256 x 256
+ * tiles and the rest on 256 x 128 tiles, split so that the tiles fill whole rounds of the
+ * CUs (one or two launches; the environment variable MMAR_LINEAR_TILE = 128 or 256 puts
+ * every column on one width, for measurements); the bits do not depend on the split. */
 int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
                      int64_t M, int64_t N, int64_t K, void* stream);
 
