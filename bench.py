@@ -31,6 +31,8 @@ its first launches; the timed steps then run at the sustained clock.
 --only fused     time only the fused block (for rocprofv3 runs)
 --only streams   time only the two-stream schedule (for a kernel-trace timeline of its
                  chunk pipeline)
+--only producer  time only the producer MatMuls (the GeLU layer of the workload's MLP and
+                 the GPT-2 QKV projection), for their kernel traces
 --only copy      one plain 1 GiB device copy, the calibration point for HBM counters
 """
 import argparse
@@ -128,7 +130,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gpt2_mlp")
-    ap.add_argument("--only", choices=["all", "fused", "streams", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "fused", "streams", "producer", "copy"], default="all")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-autotune", action="store_true",
@@ -159,6 +161,24 @@ def main():
         return
 
     w = WORKLOADS[args.workload]
+    if args.only == "producer":
+        res = {"only": "producer", "steps": args.steps}
+        for name, (mk, keys, act) in {"gelu": (make_producer_inputs(w), ("X0", "W1", "b1"), "gelu_tanh"),
+                                      "qkv": (make_qkv_inputs(WORKLOADS["gpt2_attn"]),
+                                              ("X0", "Wqkv", "bqkv"), "none")}.items():
+            pd = [torch.from_numpy(mk[k].view(np.int16)).to("cuda").view(torch.bfloat16) for k in keys]
+            H = torch.empty((pd[0].shape[0], pd[1].shape[1]), dtype=torch.bfloat16, device="cuda")
+            for _ in range(args.warmup):
+                mmar.linear(pd[0], pd[1], pd[2], act, out=H)
+            torch.cuda.synchronize()
+            med, mean = _ev_time(torch, lambda: mmar.linear(pd[0], pd[1], pd[2], act, out=H), args.steps)
+            fl = 2.0 * pd[0].shape[0] * pd[0].shape[1] * pd[1].shape[1]
+            res[name] = {"shape": [pd[0].shape[0], pd[0].shape[1], pd[1].shape[1]], "median_us": round(med * 1e3, 2),
+                         "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 2)}
+            del pd, H
+            torch.cuda.empty_cache()
+        print(json.dumps(res), flush=True)
+        return
     inp = make_inputs(w)
     d = {k: torch.from_numpy(inp[k].view(np.int16)).to("cuda").view(torch.bfloat16)
          for k in ("X", "W", "bias", "residual")}
