@@ -30,6 +30,8 @@ SCHED_AUTO, SCHED_SEQUENTIAL, SCHED_STREAMS, SCHED_PERSISTENT, SCHED_BALANCED = 
 SCHEDULES = {"auto": 0, "sequential": 1, "streams": 2, "persistent": 3, "balanced": 4}
 W_AUTO, W_DIRECT, W_PRETRANSPOSE = -1, 0, 1
 W_MODES = {"auto": -1, "direct": 0, "pretranspose": 1}
+TILE_AUTO, TILE_256x128, TILE_256x192 = -1, 0, 1
+TILES = {"auto": -1, "256x128": 0, "256x192": 1}
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -42,9 +44,9 @@ _SIGNATURES = {
     "mmar_fused": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_fused_nt": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_fused_bf16": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _P]),
-    "mmar_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32]),
+    "mmar_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32]),
     "mmar_fused_ex": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32,
-                                     _I32, _I32, _I32, _P, _SZ, _P]),
+                                     _I32, _I32, _I32, _I32, _P, _SZ, _P]),
     "mmar_transpose_weight": (ctypes.c_int, [_P, _P, _I64, _I64, _P]),
     "mmar_sequential": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32, _I32, _P]),
     "mmar_unfused": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _P]),
@@ -55,9 +57,10 @@ _SIGNATURES = {
     "mmar_gemm_partials": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, _I32, _P]),
     "mmar_reduce_epilogue_only": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _I32, _F, _U64, _P]),
     "mmar_autotune": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.c_uint32]),
-    "mmar_set_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32]),
+    "mmar_set_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32]),
     "mmar_get_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
-                                     ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32)]),
+                                     ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
+                                     ctypes.POINTER(_I32)]),
     "mmar_last_error": (ctypes.c_char_p, []),
     "mmar_version": (ctypes.c_char_p, []),
     "mmar_release": (ctypes.c_int, []),
@@ -205,13 +208,15 @@ def fused_bf16(X, W, bias, residual, P, p_drop, seed, out=None, stream=None):
 
 
 def fused_ex(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0), ring=0,
-             w_mode="auto", workspace=None, out=None, stream=None):
+             w_mode="auto", tile="auto", workspace=None, out=None, stream=None):
     """mmar_fused_ex: every choice explicit; ``workspace`` is an optional GPU tensor."""
     torch = _torch()
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
     if isinstance(w_mode, str):
         w_mode = W_MODES[w_mode]
+    if isinstance(tile, str):
+        tile = TILES[tile]
     M, N, K = _shapes(X, W, P)
     out = _out(out, (M, N), X)
     ws_ptr, ws_bytes = None, 0
@@ -223,7 +228,7 @@ def fused_ex(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0), ring
         rc = lib.mmar_fused_ex(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)), _bits(bias, "bias", (N,)),
                                _bits(residual, "residual", (M, N)), out.data_ptr(), M, N, K, int(P),
                                float(p_drop), int(seed) & (2 ** 64 - 1), int(schedule), int(chunk[0]),
-                               int(chunk[1]), int(ring), int(w_mode), ws_ptr, ws_bytes,
+                               int(chunk[1]), int(ring), int(w_mode), int(tile), ws_ptr, ws_bytes,
                                _stream(X.device, stream))
     _check(rc)
     return out
@@ -399,13 +404,15 @@ def reduce_epilogue_only(partials, bias, residual, p_drop, seed, out=None, strea
     return out
 
 
-def workspace_bytes(schedule, M, N, K, P, chunk=(0, 0), ring=0, w_mode="auto") -> int:
+def workspace_bytes(schedule, M, N, K, P, chunk=(0, 0), ring=0, w_mode="auto", tile="auto") -> int:
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
     if isinstance(w_mode, str):
         w_mode = W_MODES[w_mode]
+    if isinstance(tile, str):
+        tile = TILES[tile]
     n = lib.mmar_workspace_bytes(int(schedule), int(M), int(N), int(K), int(P), int(chunk[0]),
-                                 int(chunk[1]), int(ring), int(w_mode))
+                                 int(chunk[1]), int(ring), int(w_mode), int(tile))
     if n == 0 and last_error():
         raise MmarError(EINVAL, last_error())
     return int(n)
@@ -415,17 +422,20 @@ def autotune(M, N, K, P, flags=0) -> None:
     _check(lib.mmar_autotune(int(M), int(N), int(K), int(P), int(flags)))
 
 
-def set_plan(M, N, K, P, schedule, chunk=(0, 0), ring=0, w_mode="auto") -> None:
+def set_plan(M, N, K, P, schedule, chunk=(0, 0), ring=0, w_mode="auto", tile="auto") -> None:
     if isinstance(schedule, str):
         schedule = SCHEDULES[schedule]
     if isinstance(w_mode, str):
         w_mode = W_MODES[w_mode]
+    if isinstance(tile, str):
+        tile = TILES[tile]
     _check(lib.mmar_set_plan(int(M), int(N), int(K), int(P), int(schedule), int(chunk[0]),
-                             int(chunk[1]), int(ring), int(w_mode)))
+                             int(chunk[1]), int(ring), int(w_mode), int(tile)))
 
 
 def get_plan(M, N, K, P):
-    s, cm, cn, r, wm = _I32(), _I32(), _I32(), _I32(), _I32()
+    s, cm, cn, r, wm, t = _I32(), _I32(), _I32(), _I32(), _I32(), _I32()
     _check(lib.mmar_get_plan(int(M), int(N), int(K), int(P), ctypes.byref(s), ctypes.byref(cm),
-                             ctypes.byref(cn), ctypes.byref(r), ctypes.byref(wm)))
-    return {"schedule": s.value, "chunk": (cm.value, cn.value), "ring": r.value, "w_mode": wm.value}
+                             ctypes.byref(cn), ctypes.byref(r), ctypes.byref(wm), ctypes.byref(t)))
+    return {"schedule": s.value, "chunk": (cm.value, cn.value), "ring": r.value, "w_mode": wm.value,
+            "tile": t.value}

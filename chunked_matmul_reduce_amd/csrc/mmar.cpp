@@ -48,7 +48,11 @@ struct Plan {
     int sched = MMAR_SCHED_PERSISTENT;
     int cm = 0, cn = 0, ring = 0;
     int wmode = MMAR_W_AUTO;   // MMAR_W_DIRECT or MMAR_W_PRETRANSPOSE once resolved
+    int tile = MMAR_TILE_AUTO; // MMAR_TILE_256x128 or MMAR_TILE_256x192 once resolved: the
+                               // fused tile kernel's shape (persistent and balanced schedules)
     int hm = 0, hn = 0;        // MMAR_SCHED_BALANCED: head block [0, hm) x [0, hn) (0: none)
+    float margin_ms = 0.0f;    // autotuned plans: by how much (ms) the plan beat the default
+                               // beyond the run-to-run spread (0: the default was kept)
 };
 
 constexpr int kMaxRing = 8;
@@ -60,9 +64,12 @@ struct DevState {
     int id = -1;
     int cus = 0;
     std::string arch;
-    int occ[mmar::kNumModes][2] = {};  // tile kernel occupancy per mode and (bk == 64 ? 0 : 1)
+    // tile kernel occupancy per mode, (bk == 64 ? 0 : 1) and tile shape
+    int occ[mmar::kNumModes][2][mmar::kNumTiles] = {};
     int red_occ = 0;
-    std::mutex mu;       // serializes use of the library workspace / side stream
+    std::mutex mu;       // serializes use of the library workspace
+    std::mutex side_mu;  // serializes creation and use of the side stream and its events
+                         // (taken after mu when both are held)
     void* ws = nullptr;
     size_t ws_bytes = 0;
     hipStream_t side = nullptr;
@@ -105,12 +112,14 @@ int check_chunk(const Shape& s, int32_t cm, int32_t cn) {
     return MMAR_OK;
 }
 
-int check_sched(int32_t sched, int32_t ring, int32_t wmode) {
+int check_sched(int32_t sched, int32_t ring, int32_t wmode, int32_t tile) {
     if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_BALANCED)
         return fail(MMAR_EINVAL, "unknown schedule");
     if (ring < 0 || ring > kMaxRing) return fail(MMAR_EINVAL, "ring must be in [0, 8]");
     if (wmode < MMAR_W_AUTO || wmode > MMAR_W_PRETRANSPOSE)
         return fail(MMAR_EINVAL, "unknown weight mode");
+    if (tile < MMAR_TILE_AUTO || tile > MMAR_TILE_256x192)
+        return fail(MMAR_EINVAL, "unknown tile shape");
     return MMAR_OK;
 }
 
@@ -165,10 +174,11 @@ int current_device(DevState** out) {
         st->arch = prop.gcnArchName;
         st->cus = prop.multiProcessorCount;
         if (st->arch.compare(0, 6, "gfx950") == 0) {
-            for (int m = 0; m < mmar::kNumModes; ++m) {
-                st->occ[m][0] = mmar::tile_occupancy(m, 64);
-                st->occ[m][1] = mmar::tile_occupancy(m, 32);
-            }
+            for (int m = 0; m < mmar::kNumModes; ++m)
+                for (int t = 0; t < mmar::kNumTiles; ++t) {
+                    st->occ[m][0][t] = mmar::tile_occupancy(m, 64, t);
+                    st->occ[m][1][t] = mmar::tile_occupancy(m, 32, t);
+                }
             st->red_occ = mmar::reduce_occupancy();
         }
         it = g_dev.emplace(dev, std::move(st)).first;
@@ -197,6 +207,7 @@ int ensure_workspace(DevState* st, size_t bytes) {
     return MMAR_OK;
 }
 
+// Creates the side stream and its events once; the caller holds st->side_mu.
 int ensure_streams(DevState* st) {
     if (st->side) return MMAR_OK;
     MMAR_HIP(hipStreamCreateWithFlags(&st->side, hipStreamNonBlocking));
@@ -217,23 +228,27 @@ int default_wmode(const Shape&) { return MMAR_W_DIRECT; }
 
 constexpr int kDefaultCUs = 256;   // MI355X; used where no device has been seen yet
 
-int64_t tile_count(int64_t rows, int64_t cols) {
-    return ((rows + mmar::kBM - 1) / mmar::kBM) * ((cols + mmar::kBN - 1) / mmar::kBN);
+// Output columns of a fused-block tile (MMAR_TILE_*).
+int block_bn(int tile) { return mmar::tile_bn(mmar::kModeFused, tile); }
+
+int64_t tile_count(int64_t rows, int64_t cols, int bn) {
+    return ((rows + mmar::kBM - 1) / mmar::kBM) * ((cols + bn - 1) / bn);
 }
 
 // Head of the balanced schedule: the largest block of whole leading tile columns
-// [0, M) x [0, hn), or of whole leading tile rows [0, hm) x [0, N), whose tile count is a
-// positive multiple of g (the persistent grid, one workgroup per CU), leaving a non-empty
-// tail.  No split ({0, 0}) when the tile count already is a multiple of g or none exists.
-std::pair<int, int> balanced_split(const Shape& s, int g) {
+// [0, M) x [0, hn), or of whole leading tile rows [0, hm) x [0, N), whose tile count (of
+// bn-wide tiles) is a positive multiple of g (the persistent grid, one workgroup per CU),
+// leaving a non-empty tail.  No split ({0, 0}) when the tile count already is a multiple
+// of g or none exists.
+std::pair<int, int> balanced_split(const Shape& s, int g, int bn) {
     std::pair<int, int> best{0, 0};
-    if (g < 1 || tile_count(s.M, s.N) % g == 0) return best;
-    const int64_t tm = (s.M + mmar::kBM - 1) / mmar::kBM, tn = (s.N + mmar::kBN - 1) / mmar::kBN;
+    if (g < 1 || tile_count(s.M, s.N, bn) % g == 0) return best;
+    const int64_t tm = (s.M + mmar::kBM - 1) / mmar::kBM, tn = (s.N + bn - 1) / bn;
     int64_t best_head = 0;
     for (int64_t j = tn - 1; j >= 1; --j)
         if (tm * j >= g && (tm * j) % g == 0) {
             best_head = tm * j;
-            best = {static_cast<int>(s.M), static_cast<int>(j * mmar::kBN)};
+            best = {static_cast<int>(s.M), static_cast<int>(j * bn)};
             break;
         }
     for (int64_t i = tm - 1; i >= 1; --i)
@@ -243,6 +258,9 @@ std::pair<int, int> balanced_split(const Shape& s, int g) {
         }
     return best;
 }
+
+// The default tile shape of the fused block: 256 x 128.
+int default_tile(const Shape&) { return MMAR_TILE_256x128; }
 
 // The default plan is the persistent schedule.  The balanced schedule is left to the
 // autotuner: where the last round of tiles is partial it won on some shapes (the
@@ -257,18 +275,22 @@ Plan default_plan(const Shape& s, int) {
     p.cn = static_cast<int>(s.N);
     p.ring = 0;
     p.wmode = default_wmode(s);
+    p.tile = default_tile(s);
     return p;
 }
 
-// Fill in zero chunk sizes, ring, weight mode and the balanced schedule's head.
+// Fill in zero chunk sizes, ring, weight mode, tile and the balanced schedule's head.
+// The chunked schedules run the partials kernel, which has the 256 x 128 tile only.
 Plan resolve(const Shape& s, Plan p, int cus) {
     p.hm = p.hn = 0;
     if (p.sched == MMAR_SCHED_AUTO) p.sched = MMAR_SCHED_PERSISTENT;
+    if (p.tile == MMAR_TILE_AUTO) p.tile = default_tile(s);
+    if (p.sched == MMAR_SCHED_SEQUENTIAL || p.sched == MMAR_SCHED_STREAMS) p.tile = MMAR_TILE_256x128;
     if (p.sched == MMAR_SCHED_BALANCED) {
         p.cm = static_cast<int>(s.M);
         p.cn = static_cast<int>(s.N);
         p.ring = 0;
-        const auto sp = balanced_split(s, cus);
+        const auto sp = balanced_split(s, cus, block_bn(p.tile));
         p.hm = sp.first;
         p.hn = sp.second;
         if (p.wmode == MMAR_W_AUTO) p.wmode = default_wmode(s);
@@ -337,7 +359,8 @@ bool plan_is_valid(const Shape& s, const Plan& p) {
     const bool ring_ok = p.ring >= 0 && p.ring <= kMaxRing &&
                          (p.sched != MMAR_SCHED_STREAMS || p.ring >= 1);
     const bool w_ok = p.wmode == MMAR_W_DIRECT || p.wmode == MMAR_W_PRETRANSPOSE;
-    return shape_ok && chunk_ok && sched_ok && ring_ok && w_ok;
+    const bool tile_ok = p.tile == MMAR_TILE_256x128 || p.tile == MMAR_TILE_256x192;
+    return shape_ok && chunk_ok && sched_ok && ring_ok && w_ok && tile_ok;
 }
 
 void load_plan_cache_locked() {
@@ -351,18 +374,19 @@ void load_plan_cache_locked() {
     while (std::fgets(line, sizeof line, f)) {
         char arch[64] = {0};
         long long M, N, K;
-        int P, sched, cm, cn, ring, wmode;
+        int P, sched, cm, cn, ring, wmode, tile;
         if (std::sscanf(line,
                         " {\"arch\": \"%63[^\"]\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
                         "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d, "
-                        "\"w_mode\": %d",
-                        arch, &M, &N, &K, &P, &sched, &cm, &cn, &ring, &wmode) == 10) {
+                        "\"w_mode\": %d, \"tile\": %d",
+                        arch, &M, &N, &K, &P, &sched, &cm, &cn, &ring, &wmode, &tile) == 11) {
             Plan p;
             p.sched = sched;
             p.cm = cm;
             p.cn = cn;
             p.ring = ring;
             p.wmode = wmode;
+            p.tile = tile;
             if (plan_is_valid(Shape{M, N, K, P}, p)) g_plans[PlanKey(arch, M, N, K, P)] = p;
         }
     }
@@ -382,10 +406,11 @@ void save_plan_cache_locked() {
         std::fprintf(f,
                      " {\"arch\": \"%s\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
                      "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d, "
-                     "\"w_mode\": %d}%s\n",
+                     "\"w_mode\": %d, \"tile\": %d, \"margin_ms\": %.4f}%s\n",
                      std::get<0>(k).c_str(), (long long)std::get<1>(k), (long long)std::get<2>(k),
                      (long long)std::get<3>(k), std::get<4>(k), p.sched, p.cm, p.cn, p.ring,
-                     p.wmode, ++i < g_plans.size() ? "," : "");
+                     p.wmode, p.tile, static_cast<double>(p.margin_ms),
+                     ++i < g_plans.size() ? "," : "");
     }
     std::fprintf(f, "]\n");
     std::fclose(f);
@@ -401,7 +426,7 @@ Plan lookup_plan(const DevState* st, const Shape& s) {
 // Plan for a call: the cached / default plan (schedule AUTO) or the explicit arguments,
 // with non-zero chunk / ring arguments and a non-AUTO weight mode overriding.
 Plan plan_for(const DevState* st, const Shape& s, int32_t sched, int32_t cm, int32_t cn,
-              int32_t ring, int32_t wmode) {
+              int32_t ring, int32_t wmode, int32_t tile) {
     Plan p;
     if (sched == MMAR_SCHED_AUTO) {
         p = lookup_plan(st, s);
@@ -409,11 +434,13 @@ Plan plan_for(const DevState* st, const Shape& s, int32_t sched, int32_t cm, int
         p.sched = sched;
         p.ring = ring;
         p.wmode = MMAR_W_AUTO;
+        p.tile = MMAR_TILE_AUTO;
     }
     if (cm) p.cm = cm;
     if (cn) p.cn = cn;
     if (ring) p.ring = ring;
     if (wmode != MMAR_W_AUTO) p.wmode = wmode;
+    if (tile != MMAR_TILE_AUTO) p.tile = tile;
     return resolve(s, p, st->cus);
 }
 
@@ -443,8 +470,8 @@ int bk_for(const Shape& s) {
     return ((s.K / s.P) % 64 == 0) ? 64 : 32;
 }
 
-int grid_for(const DevState* st, int mode, int bk, int items) {
-    int occ = st->occ[mode][bk == 64 ? 0 : 1];
+int grid_for(const DevState* st, int mode, int bk, int items, int tile = mmar::kTile128) {
+    int occ = st->occ[mode][bk == 64 ? 0 : 1][tile];
     if (occ < 1) occ = 1;
     const int resident = st->cus * occ;
     return std::max(1, std::min(items, resident));
@@ -479,13 +506,15 @@ TileArgs tile_args(const Call& c, int rm0, int rn0, int RM, int RN, int cm, int 
     return a;
 }
 
-int run_persistent(const DevState* st, const Call& c, int mode, int cm, int cn, hipStream_t s) {
+int run_persistent(const DevState* st, const Call& c, int mode, int cm, int cn, hipStream_t s,
+                   int tile = mmar::kTile128) {
     const int bk = bk_for(c.s);
     TileArgs a = tile_args(c, 0, 0, static_cast<int>(c.s.M), static_cast<int>(c.s.N), cm, cn);
-    const int64_t items =
-        static_cast<int64_t>(c.s.M / cm) * (c.s.N / cn) * tiles_in(cm, cn, mmar::tile_bn(mode));
+    const int64_t items = static_cast<int64_t>(c.s.M / cm) * (c.s.N / cn) *
+                          tiles_in(cm, cn, mmar::tile_bn(mode, tile));
     a.total_items = static_cast<int32_t>(items);
-    MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, a, grid_for(st, mode, bk, a.total_items), s));
+    MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, tile, a,
+                               grid_for(st, mode, bk, a.total_items, tile), s));
     return MMAR_OK;
 }
 
@@ -497,7 +526,7 @@ int launch_partials(const DevState* st, const Call& c, int rm0, int rn0, int cm,
     const int64_t items = static_cast<int64_t>(tiles_in(cm, cn)) * c.s.P;
     if (items >= (int64_t(1) << 31)) return fail(MMAR_EINVAL, "too many work items");
     a.total_items = static_cast<int32_t>(items);
-    MMAR_HIP(mmar::launch_tile(mmar::kModePartials, bk, c.w_t, a,
+    MMAR_HIP(mmar::launch_tile(mmar::kModePartials, bk, c.w_t, mmar::kTile128, a,
                                grid_for(st, mmar::kModePartials, bk, a.total_items), s));
     return MMAR_OK;
 }
@@ -531,7 +560,12 @@ int run_chunked(DevState* st, const Call& c, const Plan& p, float* ws, hipStream
     const size_t slot_elems = static_cast<size_t>(c.s.P) * cm * cn;
     const bool two = p.sched == MMAR_SCHED_STREAMS;
     const int ring = two ? p.ring : 1;
+    // The side stream and the events are per device, shared by every call: the whole
+    // enqueue sequence of a call (its event records and waits) is done under the lock, so
+    // two calls with their own workspaces never see each other's records.
+    std::unique_lock<std::mutex> side_lock(st->side_mu, std::defer_lock);
     if (two) {
+        side_lock.lock();
         int rc = ensure_streams(st);
         if (rc) return rc;
         // earlier reductions on the side stream must be done before slots are rewritten
@@ -571,13 +605,13 @@ int run_chunked(DevState* st, const Call& c, const Plan& p, float* ws, hipStream
 // tail; the same bits as the persistent schedule (the same MFMA sequence per slice, the
 // same fixed-order fp32 reduction and epilogue).
 int run_balanced(const DevState* st, const Call& c, const Plan& p, float* ws, hipStream_t s) {
-    if (p.hm == 0) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s);
+    if (p.hm == 0) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s, p.tile);
     const int M = static_cast<int>(c.s.M), N = static_cast<int>(c.s.N);
     const int bk = bk_for(c.s);
     TileArgs a = tile_args(c, 0, 0, p.hm, p.hn, p.hm, p.hn);
-    a.total_items = static_cast<int32_t>(tiles_in(p.hm, p.hn));
-    MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, a,
-                               grid_for(st, mmar::kModeFused, bk, a.total_items), s));
+    a.total_items = static_cast<int32_t>(tiles_in(p.hm, p.hn, block_bn(p.tile)));
+    MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, p.tile, a,
+                               grid_for(st, mmar::kModeFused, bk, a.total_items, p.tile), s));
     const int tr0 = p.hm == M ? 0 : p.hm, tc0 = p.hm == M ? p.hn : 0;
     const int TM = M - tr0, TN = N - tc0;
     int rc = launch_partials(st, c, tr0, tc0, TM, TN, ws, s);
@@ -599,11 +633,13 @@ int run_with_ws(DevState* st, Call c, const Plan& p, RunKind kind, char* ws, hip
         c.W = wt;
         c.w_t = true;
     }
-    if (kind == kRunReduced) return run_persistent(st, c, mmar::kModeReduced, p.cm, p.cn, s);
+    if (kind == kRunReduced)
+        return run_persistent(st, c, mmar::kModeReduced, p.cm, p.cn, s, p.tile);
     if (kind == kRunPartials)
         return launch_partials(st, c, 0, 0, static_cast<int>(c.s.M), static_cast<int>(c.s.N),
                                c.out, s);
-    if (p.sched == MMAR_SCHED_PERSISTENT) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s);
+    if (p.sched == MMAR_SCHED_PERSISTENT)
+        return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s, p.tile);
     if (p.sched == MMAR_SCHED_BALANCED)
         return run_balanced(st, c, p, reinterpret_cast<float*>(ws + wt_bytes), s);
     return run_chunked(st, c, p, reinterpret_cast<float*>(ws + wt_bytes), s);
@@ -665,46 +701,63 @@ int check_call(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
 int fused_impl(const uint16_t* X, const uint16_t* W, bool w_t, const uint16_t* bias,
                const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                int32_t P, float p_drop, uint64_t seed, int32_t sched, int32_t chunk_m,
-               int32_t chunk_n, int32_t ring, int32_t wmode, void* workspace, size_t ws_bytes,
-               void* stream) {
+               int32_t chunk_n, int32_t ring, int32_t wmode, int32_t tile, void* workspace,
+               size_t ws_bytes, void* stream) {
     g_err.clear();
     Call c;
     const Shape s{M, N, K, P};
     int rc = check_call(X, W, bias, residual, out, s, p_drop, seed, chunk_m, chunk_n, &c);
     if (rc) return rc;
-    if ((rc = check_sched(sched, ring, wmode))) return rc;
+    if ((rc = check_sched(sched, ring, wmode, tile))) return rc;
     if (sched == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
         return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
     c.w_t = w_t;
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
-    const Plan p = plan_for(st, s, sched, chunk_m, chunk_n, ring, wmode);
+    const Plan p = plan_for(st, s, sched, chunk_m, chunk_n, ring, wmode, tile);
     return run_plan(st, c, p, kRunFused, workspace, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
 // ------------------------------------------------------------------ autotuner
-int time_plan(DevState* st, const Call& c, const Plan& p, hipStream_t s, float* ms_out) {
-    hipEvent_t e0, e1;
-    MMAR_HIP(hipEventCreate(&e0));
-    MMAR_HIP(hipEventCreate(&e1));
-    int rc = MMAR_OK;
-    for (int i = 0; i < 2 && !rc; ++i) rc = run_plan(st, c, p, kRunFused, nullptr, 0, s);
-    std::vector<float> t;
-    for (int i = 0; i < 5 && !rc; ++i) {
-        if (hipEventRecord(e0, s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
-        if (!rc) rc = run_plan(st, c, p, kRunFused, nullptr, 0, s);
-        if (!rc && hipEventRecord(e1, s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
-        if (!rc && hipEventSynchronize(e1) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventSynchronize");
-        float ms = 0;
-        if (!rc && hipEventElapsedTime(&ms, e0, e1) != hipSuccess) rc = fail(MMAR_EHIP, "elapsed");
-        t.push_back(ms);
-    }
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
-    if (rc) return rc;
+// Median and interquartile range of a sorted sample.
+void med_iqr(std::vector<float> t, float* med, float* iqr) {
     std::sort(t.begin(), t.end());
-    *ms_out = t[t.size() / 2];
-    return MMAR_OK;
+    const size_t n = t.size();
+    *med = n % 2 ? t[n / 2] : 0.5f * (t[n / 2 - 1] + t[n / 2]);
+    *iqr = t[(3 * n) / 4] - t[n / 4];
+}
+
+// Times every candidate plan `rounds` times, interleaved (round r runs every candidate once,
+// in order), so clock drift and thermal state affect all candidates alike.  times[i] gets
+// candidate i's per-call durations in ms.
+int time_plans(DevState* st, const Call& c, const std::vector<Plan>& plans, int rounds,
+               hipStream_t s, std::vector<std::vector<float>>* times) {
+    const size_t n = plans.size();
+    times->assign(n, {});
+    std::vector<hipEvent_t> ev(2 * n, nullptr);
+    int rc = MMAR_OK;
+    for (auto& e : ev)
+        if (!rc && hipEventCreate(&e) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventCreate");
+    for (size_t i = 0; i < n && !rc; ++i)   // warm-up: one call of each
+        rc = run_plan(st, c, plans[i], kRunFused, nullptr, 0, s);
+    for (int r = 0; r < rounds && !rc; ++r) {
+        for (size_t i = 0; i < n && !rc; ++i) {
+            if (hipEventRecord(ev[2 * i], s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
+            if (!rc) rc = run_plan(st, c, plans[i], kRunFused, nullptr, 0, s);
+            if (!rc && hipEventRecord(ev[2 * i + 1], s) != hipSuccess)
+                rc = fail(MMAR_EHIP, "hipEventRecord");
+        }
+        if (!rc && hipStreamSynchronize(s) != hipSuccess) rc = fail(MMAR_EHIP, "hipStreamSynchronize");
+        for (size_t i = 0; i < n && !rc; ++i) {
+            float ms = 0;
+            if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess)
+                rc = fail(MMAR_EHIP, "hipEventElapsedTime");
+            (*times)[i].push_back(ms);
+        }
+    }
+    for (auto& e : ev)
+        if (e) (void)hipEventDestroy(e);
+    return rc;
 }
 
 std::vector<int> divisors32(int64_t n, std::initializer_list<int> parts) {
@@ -728,7 +781,8 @@ int mmar_fused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                void* stream) {
     return fused_impl(X, W, false, bias, residual, out, M, N, K, P, p_drop, seed,
-                      MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_AUTO, nullptr, 0, stream);
+                      MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_AUTO, MMAR_TILE_AUTO, nullptr,
+                      0, stream);
 }
 
 int mmar_fused_nt(const uint16_t* X, const uint16_t* Wt, const uint16_t* bias,
@@ -736,7 +790,8 @@ int mmar_fused_nt(const uint16_t* X, const uint16_t* Wt, const uint16_t* bias,
                   int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                   void* stream) {
     return fused_impl(X, Wt, true, bias, residual, out, M, N, K, P, p_drop, seed,
-                      MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_DIRECT, nullptr, 0, stream);
+                      MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_DIRECT, MMAR_TILE_AUTO, nullptr,
+                      0, stream);
 }
 
 int mmar_fused_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
@@ -771,10 +826,12 @@ int mmar_fused_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
 }
 
 size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, int32_t P,
-                            int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode) {
+                            int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode,
+                            int32_t tile) {
     g_err.clear();
     const Shape s{M, N, K, P};
-    if (check_shape(s) || check_chunk(s, chunk_m, chunk_n) || check_sched(schedule, ring, w_mode))
+    if (check_shape(s) || check_chunk(s, chunk_m, chunk_n) ||
+        check_sched(schedule, ring, w_mode, tile))
         return 0;
     if (schedule == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N))) {
         fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
@@ -806,21 +863,23 @@ size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, i
         p.sched = schedule;
         p.ring = ring;
         p.wmode = MMAR_W_AUTO;
+        p.tile = MMAR_TILE_AUTO;
     }
     if (chunk_m) p.cm = chunk_m;
     if (chunk_n) p.cn = chunk_n;
     if (ring) p.ring = ring;
     if (w_mode != MMAR_W_AUTO) p.wmode = w_mode;
+    if (tile != MMAR_TILE_AUTO) p.tile = tile;
     return ws_bytes_for(s, resolve(s, p, ws_cus), false);
 }
 
 int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                   int32_t P, float p_drop, uint64_t seed, int32_t schedule, int32_t chunk_m,
-                  int32_t chunk_n, int32_t ring, int32_t w_mode, void* workspace,
+                  int32_t chunk_n, int32_t ring, int32_t w_mode, int32_t tile, void* workspace,
                   size_t ws_bytes, void* stream) {
     return fused_impl(X, W, false, bias, residual, out, M, N, K, P, p_drop, seed, schedule,
-                      chunk_m, chunk_n, ring, w_mode, workspace, ws_bytes, stream);
+                      chunk_m, chunk_n, ring, w_mode, tile, workspace, ws_bytes, stream);
 }
 
 int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
@@ -828,7 +887,8 @@ int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                     int32_t P, float p_drop, uint64_t seed, int32_t chunk_m, int32_t chunk_n,
                     void* stream) {
     return fused_impl(X, W, false, bias, residual, out, M, N, K, P, p_drop, seed,
-                      MMAR_SCHED_SEQUENTIAL, chunk_m, chunk_n, 0, MMAR_W_AUTO, nullptr, 0, stream);
+                      MMAR_SCHED_SEQUENTIAL, chunk_m, chunk_n, 0, MMAR_W_AUTO, MMAR_TILE_AUTO,
+                      nullptr, 0, stream);
 }
 
 int mmar_transpose_weight(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, void* stream) {
@@ -860,7 +920,7 @@ int mmar_gemm_only(const uint16_t* X, const uint16_t* W, float* T_out, int64_t M
     c.W = W;
     c.out = T_out;
     c.s = s;
-    Plan p = plan_for(st, s, MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_AUTO);
+    Plan p = plan_for(st, s, MMAR_SCHED_AUTO, chunk_m, chunk_n, 0, MMAR_W_AUTO, MMAR_TILE_AUTO);
     if (p.sched != MMAR_SCHED_PERSISTENT) {   // the GEMM of the persistent path
         p.sched = MMAR_SCHED_PERSISTENT;
         p.cm = chunk_m ? chunk_m : static_cast<int>(M);
@@ -885,7 +945,7 @@ int mmar_gemm_partials(const uint16_t* X, const uint16_t* W, float* partials, in
     c.W = W;
     c.out = partials;
     c.s = s;
-    const Plan p = plan_for(st, s, MMAR_SCHED_AUTO, 0, 0, 0, MMAR_W_AUTO);
+    const Plan p = plan_for(st, s, MMAR_SCHED_AUTO, 0, 0, 0, MMAR_W_AUTO, MMAR_TILE_AUTO);
     return run_plan(st, c, p, kRunPartials, nullptr, 0, static_cast<hipStream_t>(stream));
 }
 
@@ -985,7 +1045,8 @@ static int run_linear_columns(const DevState* st, const Call& c, int mode, int n
     const int M = static_cast<int>(c.s.M);
     TileArgs a = tile_args(c, 0, n0, M, cols, M, cols);
     a.total_items = static_cast<int32_t>(tiles_in(M, cols, mmar::tile_bn(mode)));
-    MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, a, grid_for(st, mode, bk, a.total_items), s));
+    MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, mmar::kTile128, a,
+                               grid_for(st, mode, bk, a.total_items), s));
     return MMAR_OK;
 }
 
@@ -1083,12 +1144,12 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
 }
 
 int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
-                  int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode) {
+                  int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode, int32_t tile) {
     g_err.clear();
     const Shape s{M, N, K, P};
     int rc;
     if ((rc = check_shape(s)) || (rc = check_chunk(s, chunk_m, chunk_n)) ||
-        (rc = check_sched(schedule, ring, w_mode)))
+        (rc = check_sched(schedule, ring, w_mode, tile)))
         return rc;
     if (schedule == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
         return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
@@ -1107,17 +1168,19 @@ int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
     p.cn = chunk_n;
     p.ring = ring;
     p.wmode = w_mode;
+    p.tile = tile;
     g_plans[key] = resolve(s, p, st->cus);
     return MMAR_OK;
 }
 
 int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
-                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring, int32_t* w_mode) {
+                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring, int32_t* w_mode,
+                  int32_t* tile) {
     g_err.clear();
     const Shape s{M, N, K, P};
     int rc;
     if ((rc = check_shape(s))) return rc;
-    if (!schedule || !chunk_m || !chunk_n || !ring || !w_mode)
+    if (!schedule || !chunk_m || !chunk_n || !ring || !w_mode || !tile)
         return fail(MMAR_EINVAL, "NULL output pointer");
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
@@ -1127,6 +1190,7 @@ int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
     *chunk_n = p.cn;
     *ring = p.ring;
     *w_mode = p.wmode;
+    *tile = p.tile;
     return MMAR_OK;
 }
 
@@ -1138,24 +1202,28 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
 
-    // candidate plans
+    // candidate plans; the first is the incumbent (the default plan)
     std::vector<Plan> cands;
-    for (int wm : {MMAR_W_DIRECT, MMAR_W_PRETRANSPOSE})
-        for (int cm : divisors32(M, {1, 2, 4}))
-            for (int cn : divisors32(N, {1, 2})) {
-                Plan p;
-                p.sched = MMAR_SCHED_PERSISTENT;
-                p.cm = cm;
-                p.cn = cn;
-                p.wmode = wm;
-                cands.push_back(p);
-            }
-    if (balanced_split(s, st->cus).first != 0)
+    cands.push_back(resolve(s, default_plan(s, st->cus), st->cus));
+    for (int tile : {MMAR_TILE_256x128, MMAR_TILE_256x192})
         for (int wm : {MMAR_W_DIRECT, MMAR_W_PRETRANSPOSE}) {
-            Plan p;
-            p.sched = MMAR_SCHED_BALANCED;
-            p.wmode = wm;
-            cands.push_back(p);
+            for (int cm : divisors32(M, {1, 2, 4}))
+                for (int cn : divisors32(N, {1, 2})) {
+                    Plan p;
+                    p.sched = MMAR_SCHED_PERSISTENT;
+                    p.cm = cm;
+                    p.cn = cn;
+                    p.wmode = wm;
+                    p.tile = tile;
+                    cands.push_back(resolve(s, p, st->cus));
+                }
+            if (balanced_split(s, st->cus, block_bn(tile)).first != 0) {
+                Plan p;
+                p.sched = MMAR_SCHED_BALANCED;
+                p.wmode = wm;
+                p.tile = tile;
+                cands.push_back(resolve(s, p, st->cus));
+            }
         }
     if (flags & 1u) {
         for (int cm : divisors32(M, {2, 4, 8, 16}))
@@ -1166,12 +1234,12 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
                 p.cn = static_cast<int>(N);
                 p.ring = r;
                 p.wmode = default_wmode(s);
-                cands.push_back(p);
+                cands.push_back(resolve(s, p, st->cus));
             }
         Plan p;
         p.sched = MMAR_SCHED_SEQUENTIAL;
         p.wmode = default_wmode(s);
-        cands.push_back(p);
+        cands.push_back(resolve(s, p, st->cus));
     }
 
     // library-owned inputs with the value spread of the block's inputs
@@ -1211,25 +1279,31 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
     c.w_t = false;
     drop_params(0.1f, 1234, &c.drop);
 
-    Plan best;
-    float best_ms = 1e30f;
-    for (Plan p : cands) {
-        p = resolve(s, p, st->cus);
-        float ms = 0;
-        rc = time_plan(st, c, p, stream, &ms);
-        if (rc) {
-            cleanup();
-            return rc;
-        }
-        if (ms < best_ms) {
-            best_ms = ms;
-            best = p;
+    // Noise-aware choice: every candidate timed kTuneRounds times, interleaved; a
+    // challenger replaces the incumbent only if its median is lower by more than the
+    // larger of the two interquartile ranges (a win inside the run-to-run spread would
+    // flip from one run or box to the next).  The best such challenger wins.
+    constexpr int kTuneRounds = 25;
+    std::vector<std::vector<float>> times;
+    rc = time_plans(st, c, cands, kTuneRounds, stream, &times);
+    cleanup();
+    if (rc) return rc;
+    std::vector<float> med(cands.size()), iqr(cands.size());
+    for (size_t i = 0; i < cands.size(); ++i) med_iqr(times[i], &med[i], &iqr[i]);
+    size_t best = 0;
+    float margin = 0.0f;
+    for (size_t i = 1; i < cands.size(); ++i) {
+        const float need = std::max(iqr[0], iqr[i]);
+        if (med[i] < med[0] - need && med[i] < med[best]) {
+            best = i;
+            margin = med[0] - med[i] - need;
         }
     }
-    cleanup();
     std::lock_guard<std::mutex> lk(g_mu);
     load_plan_cache_locked();
-    g_plans[PlanKey(st->arch, M, N, K, P)] = best;
+    Plan chosen = cands[best];
+    chosen.margin_ms = margin;
+    g_plans[PlanKey(st->arch, M, N, K, P)] = chosen;
     save_plan_cache_locked();
     return MMAR_OK;
 }
@@ -1246,6 +1320,7 @@ int mmar_release(void) {
     for (auto& kv : g_dev) {
         DevState* st = kv.second.get();
         std::lock_guard<std::mutex> dl(st->mu);
+        std::lock_guard<std::mutex> sl(st->side_mu);
         if (hipSetDevice(st->id) != hipSuccess) continue;
         (void)hipDeviceSynchronize();
         if (st->ws) (void)hipFree(st->ws);

@@ -81,11 +81,30 @@ struct AdamArgs {
 constexpr int kBM = 256;   // output rows per tile
 constexpr int kBN = 128;   // output columns per tile
 constexpr int kBNWide = 256;   // output columns per tile of kModeLinearWide
-constexpr int tile_bn(int mode) { return mode == kModeLinearWide ? kBNWide : kBN; }
 
-// Launchers (tile_kernel.hip, reduce_kernels.hip).  bk is 64 or 32 (the K step; it must divide Ks;
-// kModeLinearWide always steps by 32).  wt: a.W holds W^T [N, K] instead of W [K, N].
-hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, hipStream_t s);
+// Tile shapes of the block's modes (kModeFused, kModeReduced): the plan's choice.
+enum TileShape : int {
+    kTile128 = 0,   // 256 x 128: 8 waves of 64 x 64 at BK = 64 (4 waves of 64 x 128 at BK = 32)
+    kTile192 = 1,   // 256 x 192: 4 waves of 128 x 96, BK = 32
+};
+constexpr int kNumTiles = 2;
+constexpr int kBN192 = 192;
+// Output columns per tile of a mode on a tile shape (the partials and producer modes
+// have one shape each).
+constexpr int tile_bn(int mode, int tile = kTile128) {
+    return mode == kModeLinearWide ? kBNWide
+           : (tile == kTile192 && (mode == kModeFused || mode == kModeReduced)) ? kBN192
+                                                                               : kBN;
+}
+constexpr bool tile_supported(int mode, int tile) {
+    return tile == kTile128 || mode == kModeFused || mode == kModeReduced;
+}
+
+// Launchers (tile_kernel.hip, reduce_kernels.hip).  bk is 64 or 32 (the K step; it must
+// divide Ks; kModeLinearWide and kTile192 always step by 32).  wt: a.W holds W^T [N, K]
+// instead of W [K, N].  tile: a TileShape that tile_supported(mode, tile) accepts.
+hipError_t launch_tile(int mode, int bk, bool wt, int tile, const TileArgs& a, int grid,
+                       hipStream_t s);
 hipError_t launch_transpose(const uint16_t* W, uint16_t* Wt, int64_t K, int64_t N, hipStream_t s);
 hipError_t launch_reduce_epilogue(const ReduceArgs& a, int grid, hipStream_t s);
 hipError_t launch_fill_bf16(uint16_t* p, int64_t n, uint32_t salt, float amp, hipStream_t s);
@@ -96,8 +115,9 @@ hipError_t launch_adam(const AdamArgs& a, int grid, hipStream_t s);
 hipError_t launch_unfused_tail(const float* ws, float* T, const uint16_t* bias,
                                const uint16_t* residual, float* out, uint8_t* mask, int64_t M,
                                int64_t N, int32_t P, const DropParams& d, int grid, hipStream_t s);
-// Workgroups of the tile kernel that fit on one CU at once (0 on error).
-int tile_occupancy(int mode, int bk);
+// Workgroups of the tile kernel that fit on one CU at once (0 on error or for a shape
+// the mode does not have).
+int tile_occupancy(int mode, int bk, int tile);
 int reduce_occupancy();
 
 }  // namespace mmar

@@ -66,49 +66,87 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // registers over all its K steps (the fused block 5-6 % faster, the producer MatMul 2-4 %
 // faster than with 4 waves); 4 (one per SIMD) for the partials mode, whose work items are
 // one slice long (12 % slower with 8 waves), and at BK = 32, where a W stage has too few
-// 16-byte chunks for 8 waves to copy them in pairs.
-constexpr int tile_waves(int mode, int bk) {
-    return mode == kModeLinearWide ? 8 : bk != 64 || mode == kModePartials ? 4 : 8;
+// 16-byte chunks for 8 waves to copy them in pairs.  The 256 x 192 tile has 4 waves, one
+// per SIMD, each holding a 128 x 96 block: its slice sum and running total take 384 of
+// the 512 registers a lone wave has.
+constexpr int tile_waves(int mode, int bk, int tile) {
+    return tile == kTile192 ? 4
+           : mode == kModeLinearWide ? 8
+           : bk != 64 || mode == kModePartials ? 4 : 8;
 }
-// K step of a mode's kernel: the wide producer tile always steps by 32 (two 64-deep
-// stages of a 256 x 256 tile would not fit the LDS with copies two steps ahead).
-constexpr int tile_bk(int mode, int bk) { return mode == kModeLinearWide ? 32 : bk; }
+// K step of a mode's kernel: the wide producer tile and the 256 x 192 tile always step by
+// 32 (two 64-deep stages of either would not fit the LDS with copies two steps ahead).
+constexpr int tile_bk(int mode, int bk, int tile) {
+    return (mode == kModeLinearWide || tile == kTile192) ? 32 : bk;
+}
 constexpr bool is_linear(int mode) { return mode == kModeLinear || mode == kModeLinearWide; }
 
-template <int BK, int NW_, int BN_ = kBN>
-struct TileCfg {
+template <int BK, int NW_, int BN_, int WM_, int LEAD_, int XSTAGES_, int WSTAGES_,
+          int TLDS_ = 0>
+struct TileCfgT {
     static constexpr int BM = kBM, BN = BN_;
     static constexpr int NW = NW_;
     static constexpr int THREADS = 64 * NW;
-    static constexpr int WM = 4;                        // waves along m
+    static constexpr int WM = WM_;                      // waves along m
     static constexpr int WN = NW / WM;                  // waves along n
     static constexpr int RW = BM / WM, CW = BN / WN;    // rows / columns of a wave
     static constexpr int MB = RW / 32, NB = CW / 32;    // 32 x 32 MFMA blocks of a wave
     static constexpr int KS = BK / 16;                  // MFMA k steps per K step
-    static constexpr int LEAD = BK == 64 ? 2 : BN == 256 ? 3 : 5;   // copies run LEAD K
-                                                                    // steps ahead
-    static constexpr int XSTAGES = LEAD + 1;            // X ring depth
-    static constexpr int WSTAGES = LEAD + 2;            // W ring depth (one more than X:
-                                                        // W copies never reuse the stage
-                                                        // of the step just read)
+    static constexpr int LEAD = LEAD_;                  // copies run LEAD K steps ahead
+    static constexpr int XSTAGES = XSTAGES_;            // X ring depth
+    static constexpr int WSTAGES = WSTAGES_;            // W ring depth
     static constexpr int XS = BM * BK;                  // elements of an X stage [BM][BK]
     static constexpr int WS = BK * BN;                  // elements of a W stage [BK][BN]
     static constexpr int CPR = BK / 8;                  // 16-byte chunks per X row
     static constexpr int XQ = XS / 8 / 64 / NW;         // X copy instructions per wave
     static constexpr int WQ = WS / 8 / 64 / NW;         // W copy instructions per wave
     static constexpr int DMA = XQ + WQ;                 // copy instructions per wave per step
-    static constexpr int LDS_BYTES = (XSTAGES * XS + WSTAGES * WS) * 2;
+    // copy operations per wave per step: X copies in pairs, W copies in pairs and, when
+    // their count is odd, one single copy
+    static constexpr int XOPS = XQ / 2, WOPS = (WQ + 1) / 2, OPS = XOPS + WOPS;
+    // running-total blocks of a wave kept in LDS (after the rings), 32 x 32 fp32 each
+    static constexpr int TLDS = TLDS_;
+    static constexpr int RING_BYTES = (XSTAGES * XS + WSTAGES * WS) * 2;
+    static constexpr int LDS_BYTES = RING_BYTES + NW * TLDS * 4096;
     static_assert(LDS_BYTES <= 163840, "LDS budget");
     static_assert(MB * NB * NW * 1024 == BM * BN, "the waves' 32 x 32 blocks cover the tile");
-    static_assert(XQ % 2 == 0 && WQ % 2 == 0, "copies go in pairs");
+    static_assert(XQ % 2 == 0, "X copies go in pairs");
+    static_assert(XQ * NW * 64 * 8 == XS && WQ * NW * 64 * 8 == WS, "copies cover a stage");
+    static_assert(XSTAGES >= LEAD + 1 && WSTAGES >= LEAD + 1, "ring depth");
 };
 
-// 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).
+// The configuration of a (mode, K step, tile shape).  The 256 x 128 and wide shapes keep
+// one W stage more than X (their copies never reuse the stage of the step just read).
+// The 256 x 192 tile uses LEAD + 1 = 4 stages of each (the step handshake waits for this
+// wave's LDS reads, so the stage read last is free once every wave has passed it), the
+// copies 3 steps (about 2000 cycles) ahead, and keeps 3 of each wave's 12 running-total
+// blocks in the remaining 48 KB of LDS: with all 12 in registers the slice sum (192
+// accumulation registers), the running total (192) and the operand fragments do not fit
+// the 512 registers of a wave.
+template <int MODE, int BK, int TILE>
+struct TileCfgOf {
+    static constexpr int NW = tile_waves(MODE, BK, TILE);
+    static constexpr int BN = tile_bn(MODE, TILE);
+    static constexpr int LEAD = TILE == kTile192 ? 3 : BK == 64 ? 2 : BN == 256 ? 3 : 5;
+    using type = TileCfgT<BK, NW, BN, TILE == kTile192 ? 2 : 4, LEAD, LEAD + 1,
+                          TILE == kTile192 ? LEAD + 1 : LEAD + 2, TILE == kTile192 ? 3 : 0>;
+};
+
+// 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).  X stage rows are BK
+// elements; W stage rows are BN elements.  The LDS transpose read of W takes, per
+// half-wave, 64 bytes from each of 4 consecutive k rows: with 256- or 512-byte rows the
+// four start on the same bank, so 64-byte groups are rotated by k mod 4; with 384-byte
+// rows (BN = 192) rows k and k + 1 already sit half a bank cycle apart, so only k / 2
+// mod 2 flips the 64-byte group (an XOR inside aligned 8-chunk groups: 24 chunks per
+// row stay in range).
 template <int BK>
 __device__ __forceinline__ int swz_x(int m) {
     return BK == 64 ? ((m & 7) ^ ((m >> 3) & 1)) : ((m >> 2) & 3);
 }
-__device__ __forceinline__ int swz_w(int k) { return 4 * (k & 3); }
+template <int BN>
+__device__ __forceinline__ int swz_w(int k) {
+    return BN == 192 ? 4 * ((k >> 1) & 1) : 4 * (k & 3);
+}
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding).
 #define MMAR_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | 0x70 | 0xF00 | ((((n) >> 4) & 3) << 14))
@@ -140,6 +178,21 @@ __device__ __forceinline__ void dma16x2(const void* sbase, uint32_t voff0, uint3
         : "memory");
 }
 
+// One 16-byte global -> LDS copy per lane: reads sbase + voff, lands at lds_addr + 16 lane
+// (lds_addr wave-uniform).  M0 is saved and restored.
+__device__ __forceinline__ void dma16x1(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voff), "s"(sbase), "s"(lds_addr)
+        : "memory");
+}
+
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
@@ -156,14 +209,25 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // across it.
 __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
+// Calls f(integral_constant<int, I>) for I = B .. E-1 in order (compile-time indices for
+// register arrays).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // WT = false: W is [K, N] (n contiguous) and its MFMA operand is read with the LDS
 // transpose read; WT = true: W is given transposed, [N, K] (k contiguous, the layout of
 // a Linear layer's weight), and both operands use plain 16-byte LDS reads.
-template <int MODE, int BK, bool WT>
-__global__ __launch_bounds__(64 * tile_waves(MODE, BK))
-__attribute__((amdgpu_waves_per_eu(tile_waves(MODE, BK) / 4, tile_waves(MODE, BK) / 4)))
+template <int MODE, int BK, bool WT, int TILE>
+__global__ __launch_bounds__(64 * tile_waves(MODE, BK, TILE))
+__attribute__((amdgpu_waves_per_eu(tile_waves(MODE, BK, TILE) / 4,
+                                   tile_waves(MODE, BK, TILE) / 4)))
 void tile_kernel(TileArgs a) {
-    using C = TileCfg<BK, tile_waves(MODE, BK), tile_bn(MODE)>;
+    using C = typename TileCfgOf<MODE, BK, TILE>::type;
     // one slice and no running total: the wide producer tile stores S itself
     constexpr bool NO_T = MODE == kModeLinearWide || MODE == kModePartials;
     constexpr int BM = C::BM, BN = C::BN, NB = C::NB, MB = C::MB, KS = C::KS;
@@ -234,12 +298,14 @@ void tile_kernel(TileArgs a) {
                 const int r = idx / C::CPR, pos = idx % C::CPR;
                 const int c = pos ^ swz_x<BK>(r);
                 woff[q] = static_cast<uint32_t>(
-                    (static_cast<int64_t>(min(r, cols - 1)) * a.K + 8 * c) * 2 + (q % 2 == 0 ? 1024 : 0));
+                    (static_cast<int64_t>(min(r, cols - 1)) * a.K + 8 * c) * 2 +
+                    (q % 2 == 0 && q + 1 < C::WQ ? 1024 : 0));
             } else {
                 const int k = idx / (BN / 8), pos = idx % (BN / 8);
-                const int c = pos ^ swz_w(k);
+                const int c = pos ^ swz_w<BN>(k);
                 woff[q] = static_cast<uint32_t>(
-                    (static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2 + (q % 2 == 0 ? 1024 : 0));
+                    (static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2 +
+                    (q % 2 == 0 && q + 1 < C::WQ ? 1024 : 0));
             }
         }
         const int nsteps = (p_hi - p_lo) * sps;
@@ -259,57 +325,69 @@ void tile_kernel(TileArgs a) {
                                                      static_cast<uint32_t>(st) * step_b);
         };
 
-        // copies i and i+1 (i even; XQ and WQ are even, so a pair never mixes X and W)
-        auto copy2 = [&](int st, int i) {
-            if (i < C::XQ) {
+        // copy operation j of step st: X copies 2j, 2j+1 (j < XOPS), else W copies q, q+1
+        // (q = 2 (j - XOPS)), or W copy q alone when it is the last of an odd count
+        auto copy_op = [&](int st, int j) {
+            if (j < C::XOPS) {
+                const int i = 2 * j;
                 const uint32_t xd = lds_addr(xs_base + xstage(st) * C::XS +
                                              (C::XQ * uwave + i + 1) * 512);
                 dma16x2(step_ptr(xbase, st, xstep_b), xoff[i], xoff[i + 1], xd);
             } else {
-                const int q = i - C::XQ;
-                const uint32_t wd = lds_addr(ws_base + wstage(st) * C::WS +
-                                             (C::WQ * uwave + q + 1) * 512);
-                dma16x2(step_ptr(wbase, st, wstep_b), woff[q], woff[q + 1], wd);
+                const int q = 2 * (j - C::XOPS);
+                if (q + 1 < C::WQ) {
+                    const uint32_t wd = lds_addr(ws_base + wstage(st) * C::WS +
+                                                 (C::WQ * uwave + q + 1) * 512);
+                    dma16x2(step_ptr(wbase, st, wstep_b), woff[q], woff[q + 1], wd);
+                } else {
+                    const uint32_t wd = lds_addr(ws_base + wstage(st) * C::WS +
+                                                 (C::WQ * uwave + q) * 512);
+                    dma16x1(step_ptr(wbase, st, wstep_b), woff[q], wd);
+                }
             }
         };
 
+        // S: this slice's sums; T: the running total (the 256 x 192 tile defines T at the
+        // end of the first slice, T = 0 + S_0, so it is not cleared here)
         f32x16 S[NB][MB], T[NB][MB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 S[nb][mb] = f32x16{};
-                T[nb][mb] = f32x16{};
+                if constexpr (TILE != kTile192) T[nb][mb] = f32x16{};
             }
 
         const int last = nsteps - 1;
-        // operand fragments of MFMA k step s of K step t
-        auto frags = [&](int t, int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
+        // operand fragment of row block mb (X) / column block nb (W) for MFMA k step s of
+        // K step t
+        auto read_x = [&](int t, int s, int mb) -> bf16x8 {
             const uint16_t* xs = xs_base + xstage(t) * C::XS;
+            const int m = C::RW * wm + 32 * mb + l32;
+            return *reinterpret_cast<const bf16x8*>(xs + xrd[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
+        };
+        auto read_w = [&](int t, int s, int nb) -> bf16x8 {
             const uint16_t* wsb = ws_base + wstage(t) * C::WS;
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-                const int m = C::RW * wm + 32 * mb + l32;
-                xf[mb] = *reinterpret_cast<const bf16x8*>(
-                    xs + xrd[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
+            if constexpr (WT) {
+                const int n = C::CW * wn + 32 * nb + l32;
+                return *reinterpret_cast<const bf16x8*>(wsb + n * BK +
+                                                        8 * ((2 * s + h) ^ swz_x<BK>(n)));
+            } else {
+                const int k1 = 16 * s + wk, k2 = k1 + 4;
+                const int n = wcn + 32 * nb;
+                const uint16_t* p1 = wsb + k1 * BN + 8 * ((n >> 3) ^ swz_w<BN>(k1)) + (n & 7);
+                const uint16_t* p2 = wsb + k2 * BN + 8 * ((n >> 3) ^ swz_w<BN>(k2)) + (n & 7);
+                const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p1);
+                const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p2);
+                const v4i16 both[2] = {lo, hi};
+                return __builtin_bit_cast(bf16x8, both);
             }
+        };
+        auto frags = [&](int t, int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                if constexpr (WT) {
-                    const int n = C::CW * wn + 32 * nb + l32;
-                    wf[nb] = *reinterpret_cast<const bf16x8*>(
-                        wsb + n * BK + 8 * ((2 * s + h) ^ swz_x<BK>(n)));
-                } else {
-                    const int k1 = 16 * s + wk, k2 = k1 + 4;
-                    const int n = wcn + 32 * nb;
-                    const uint16_t* p1 = wsb + k1 * BN + 8 * ((n >> 3) ^ swz_w(k1)) + (n & 7);
-                    const uint16_t* p2 = wsb + k2 * BN + 8 * ((n >> 3) ^ swz_w(k2)) + (n & 7);
-                    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p1);
-                    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MMAR_LDS v4i16*)p2);
-                    const v4i16 both[2] = {lo, hi};
-                    wf[nb] = __builtin_bit_cast(bf16x8, both);
-                }
-            }
+            for (int mb = 0; mb < MB; ++mb) xf[mb] = read_x(t, s, mb);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) wf[nb] = read_w(t, s, nb);
         };
         // Step-boundary handshake for K step t: this wave's copies of t are done (only the
         // copies of the LEAD - 1 following steps may remain) and the barrier makes every
@@ -325,15 +403,115 @@ void tile_kernel(TileArgs a) {
 #pragma unroll
         for (int d = 0; d < C::LEAD; ++d)
 #pragma unroll
-            for (int i = 0; i < C::DMA; i += 2) copy2(min(d, last), i);
+            for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), j);
         handshake();
 
+        // running-total blocks (nb = NB - 1, mb < TLDS) kept in this wave's LDS area (the
+        // 256 x 192 tile): value 4q + j of lane l at float offset 256 (4 blk + q) + 4 l + j
+        float* const tl = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) +
+                                                   C::RING_BYTES) +
+                          uwave * C::TLDS * 1024;
+        auto in_lds = [](int nb, int mb) { return nb == NB - 1 && mb < C::TLDS; };
+
+        int st = 0;
+        if constexpr (TILE == kTile192) {
+            // 256 x 192 tile, 4 waves of 128 x 96, K steps of 32 (two MFMA k steps).
+            // MFMAs go row block by row block (mb outer); an X fragment is re-read for the
+            // next k step as soon as the three MFMAs of its row block are issued, the W
+            // fragments of the next k step are read into the other half of a double buffer
+            // at the start of a k step.  All copies of step st + LEAD go between the MFMAs
+            // of the first k step, the handshake before the second.
+            static_assert(KS == 2, "the 256 x 192 tile steps K by 32");
+            bf16x8 xf[MB], wf0[NB], wf1[NB];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) xf[mb] = read_x(0, 0, mb);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) wf0[nb] = read_w(0, 0, nb);
+
+            auto kstep192 = [&](auto zero_tag) {
+                constexpr bool ZERO = decltype(zero_tag)::value;
+                const int st2 = min(st + C::LEAD, last);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) wf1[nb] = read_w(st, 1, nb);
+                int c = 0;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            wf0[nb], xf[mb], ZERO ? f32x16{} : S[nb][mb], 0, 0, 0);
+                        const int upto = ((mb * NB + nb + 1) * C::OPS + NB * MB - 1) / (NB * MB);
+                        while (c < upto) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            copy_op(st2, c);
+                            c += 1;
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    xf[mb] = read_x(st, 1, mb);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                handshake();
+                const int nx = min(st + 1, last);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) wf0[nb] = read_w(nx, 0, nb);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+                        S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf1[nb], xf[mb],
+                                                                            S[nb][mb], 0, 0, 0);
+                    xf[mb] = read_x(nx, 0, mb);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+
+            // T = 0 + S_0 after the first slice, then T + S_1, T + S_2, ... (fp32, nearest
+            // even), in registers or in this wave's LDS area; one block at a time (the
+            // barriers keep the compiler from reading every slice sum out of the
+            // accumulation registers at once)
+            auto update = [&](auto first_tag) {
+                constexpr bool FIRST = decltype(first_tag)::value;
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        __builtin_amdgcn_sched_barrier(0);
+                        if (in_lds(nb, mb)) {
+                            float4* q = reinterpret_cast<float4*>(tl + 1024 * mb) + lane;
+#pragma unroll
+                            for (int g = 0; g < 4; ++g) {
+                                const float4 t = FIRST ? make_float4(0.f, 0.f, 0.f, 0.f) : q[64 * g];
+                                q[64 * g] = make_float4(t.x + S[nb][mb][4 * g],
+                                                        t.y + S[nb][mb][4 * g + 1],
+                                                        t.z + S[nb][mb][4 * g + 2],
+                                                        t.w + S[nb][mb][4 * g + 3]);
+                            }
+                        } else if (FIRST) {
+                            T[nb][mb] = f32x16{} + S[nb][mb];
+                        } else {
+                            T[nb][mb] += S[nb][mb];
+                        }
+                    }
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            for (int p = p_lo; p < p_hi; ++p) {
+                kstep192(std::true_type{});
+                ++st;
+                for (int j = 1; j < sps; ++j, ++st) kstep192(std::false_type{});
+                if constexpr (!NO_T) {
+                    if (p == p_lo)
+                        update(std::true_type{});
+                    else
+                        update(std::false_type{});
+                }
+            }
+        } else {
         // fragments are double-buffered: k step s of any K step uses buffer s % 2 (KS is
         // even), and the first fragments of step t+1 are read during the last MFMAs of t
         bf16x8 xa[MB], wa[NB], xb2[MB], wb2[NB];
         frags(0, 0, xa, wa);
 
-        int st = 0;
         // One K step (step st): KS k steps of NB x MB MFMAs, the copies of step st+LEAD between
         // them, the step-boundary handshake before the last k step.  ZERO marks the first
         // K step of a slice: its first k step gives the MFMAs a zero accumulator input,
@@ -343,8 +521,8 @@ void tile_kernel(TileArgs a) {
             // copies of step st+LEAD (the last steps re-copy the last one: identical bytes,
             // no branch), spread over the MFMAs of k steps 0 .. KS-2
             const int st2 = min(st + C::LEAD, last);
-            // the NB x MB MFMAs of one k step, with copies c0 .. c1-1 issued between them (all of
-            // them: the caller passes c1 - c0 <= DMA)
+            // the NB x MB MFMAs of one k step, with copy operations c0 .. c1-1 issued between
+            // them (all of them: the caller passes c1 - c0 <= OPS)
             auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1,
                              bool zero) {
                 int c = c0;
@@ -359,27 +537,27 @@ void tile_kernel(TileArgs a) {
                             c0 + ((nb * MB + mb + 1) * (c1 - c0) + NB * MB - 1) / (NB * MB);
                         while (c < upto) {
                             __builtin_amdgcn_sched_barrier(0);
-                            copy2(st2, c);
-                            c += 2;
+                            copy_op(st2, c);
+                            c += 1;
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
             };
-            constexpr int CPS = (C::DMA + KS - 2) / (KS - 1);   // copies per k step
+            constexpr int CPS = (C::OPS + KS - 2) / (KS - 1);   // copy operations per k step
 #pragma unroll
             for (int s = 0; s < KS; s += 2) {
                 // k step s (buffer a), prefetching s+1 into buffer b
                 frags(st, s + 1, xb2, wb2);
-                mfmas(xa, wa, min(s * CPS, C::DMA), min((s + 1) * CPS, C::DMA), ZERO && s == 0);
+                mfmas(xa, wa, min(s * CPS, C::OPS), min((s + 1) * CPS, C::OPS), ZERO && s == 0);
                 // k step s+1 (buffer b), prefetching s+2, or the next K step's first
                 if (s + 2 < KS) {
                     frags(st, s + 2, xa, wa);
-                    mfmas(xb2, wb2, min((s + 1) * CPS, C::DMA), min((s + 2) * CPS, C::DMA),
+                    mfmas(xb2, wb2, min((s + 1) * CPS, C::OPS), min((s + 2) * CPS, C::OPS),
                           false);
                 } else {
                     handshake();
                     frags(min(st + 1, last), 0, xa, wa);
-                    mfmas(xb2, wb2, C::DMA, C::DMA, false);
+                    mfmas(xb2, wb2, C::OPS, C::OPS, false);
                 }
             }
         };
@@ -397,6 +575,7 @@ void tile_kernel(TileArgs a) {
                   for (int mb = 0; mb < MB; ++mb) T[nb][mb] += S[nb][mb];
           }
         }
+        }
         MMAR_WAIT_VM_LDS(0);
         wg_barrier();   // every wave is done with the LDS ring (its copies landed, its reads
                         // returned) before the next item's copies
@@ -409,7 +588,70 @@ void tile_kernel(TileArgs a) {
         // arithmetic) instead of one load latency per output group.
         auto col_ok = [&](int nb) { return C::CW * wn + 32 * nb < cols; };
         auto row_ok = [&](int mb) { return C::RW * wm + 32 * mb < rows; };
-        if constexpr (is_linear(MODE)) {
+        if constexpr (TILE == kTile192) {
+            // One 32 x 32 block at a time (nb outer), the residual loads of the block PF
+            // blocks ahead in flight and the bias of a column block loaded once; the
+            // barriers keep the compiler from issuing every load (and holding every address)
+            // of the 128 x 96 wave block at once, which would not fit beside T.  fp32
+            // output only (a second, bf16 store path alone made the registers spill; the
+            // bf16-output block uses the 256 x 128 tile).  Per lane: row m_lane + 32 mb,
+            // columns n_lane + 32 nb + 8 g + 0..3.
+            constexpr int NBLK = NB * MB, PF = 3;
+            const int64_t m_lane = static_cast<int64_t>(m0) + C::RW * wm + l32;
+            const int n_lane = n0 + C::CW * wn + 4 * h;
+            uint2 bq[4], rq[PF][4];
+            // columns 8 g .. 8 g + 3 of block (nb, mb) of T, from registers or LDS
+            auto tval = [&](int nb, int mb, int g) -> float4 {
+                if (in_lds(nb, mb))
+                    return reinterpret_cast<const float4*>(tl + 1024 * mb)[64 * g + lane];
+                const f32x16& acc = T[nb][mb];
+                return make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+            };
+            // column offset of block nb (clamped into the tile), relative to n_lane
+            auto ncol = [&](int nb) { return min(C::CW * wn + 32 * nb, cols - 32) - C::CW * wn; };
+            auto issue = [&](auto ic) {   // residual loads of block i (clamped into the tile)
+                constexpr int i = decltype(ic)::value, nb = i / MB, mb = i % MB;
+                const int ml = min(C::RW * wm + 32 * mb, rows - 32) - C::RW * wm;
+                const uint16_t* rp = a.residual + (m_lane + ml) * a.N + n_lane + ncol(nb);
+#pragma unroll
+                for (int g = 0; g < 4; ++g) rq[i % PF][g] = *reinterpret_cast<const uint2*>(rp + 8 * g);
+            };
+            if constexpr (MODE == kModeFused) static_for<0, PF>(issue);
+            static_for<0, NBLK>([&](auto ic) {
+                constexpr int i = decltype(ic)::value, nb = i / MB, mb = i % MB;
+                __builtin_amdgcn_sched_barrier(0);
+                const bool ok = col_ok(nb) && row_ok(mb);
+                const int64_t m = m_lane + 32 * mb;
+                if constexpr (MODE == kModeFused) {
+                    if constexpr (mb == 0) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g)
+                            bq[g] = *reinterpret_cast<const uint2*>(a.bias + n_lane + ncol(nb) + 8 * g);
+                    }
+                    uint2 r0[4];
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) r0[g] = rq[i % PF][g];
+                    if constexpr (i + PF < NBLK) issue(std::integral_constant<int, i + PF>{});
+                    if (ok) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int64_t e = m * a.N + n_lane + 32 * nb + 8 * g;
+                            *reinterpret_cast<float4*>(a.out + e) =
+                                epilogue4(tval(nb, mb, g), bq[g], r0[g], e, a.drop);
+                        }
+                    }
+                } else {   // kModeReduced: T itself
+                    if (ok) {
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int64_t e = m * a.N + n_lane + 32 * nb + 8 * g;
+                            *reinterpret_cast<float4*>(a.out + e) = tval(nb, mb, g);
+                        }
+                    }
+                }
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (is_linear(MODE)) {
             uint2 bb[NB][4];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -512,9 +754,9 @@ void tile_kernel(TileArgs a) {
 }
 
 // ------------------------------------------------------------------ launchers
-template <int MODE, int BK, bool WT>
+template <int MODE, int BK, bool WT, int TILE>
 static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
-    using C = TileCfg<BK, tile_waves(MODE, BK), tile_bn(MODE)>;
+    using C = typename TileCfgOf<MODE, BK, TILE>::type;
     constexpr int lds = C::LDS_BYTES;
     // the dynamic-LDS limit is raised once per device (bit d of the mask: device d)
     static std::atomic<uint64_t> attr_set{0};
@@ -522,58 +764,72 @@ static hipError_t launch_tile_t(const TileArgs& a, int grid, hipStream_t s) {
     if (hipGetDevice(&dev) != hipSuccess) return hipGetLastError();
     const uint64_t bit = dev < 64 ? uint64_t(1) << dev : 0;
     if (!bit || !(attr_set.load(std::memory_order_acquire) & bit)) {
-        void (*fn)(TileArgs) = tile_kernel<MODE, BK, WT>;
+        void (*fn)(TileArgs) = tile_kernel<MODE, BK, WT, TILE>;
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_set.fetch_or(bit, std::memory_order_release);
     }
-    hipLaunchKernelGGL((tile_kernel<MODE, BK, WT>), dim3(grid), dim3(C::THREADS), lds, s, a);
+    hipLaunchKernelGGL((tile_kernel<MODE, BK, WT, TILE>), dim3(grid), dim3(C::THREADS), lds, s,
+                       a);
     return hipGetLastError();
 }
 
 template <bool WT>
-static hipError_t launch_tile_w(int mode, int bk, const TileArgs& a, int grid, hipStream_t s) {
-    if (mode == kModeLinearWide) return launch_tile_t<kModeLinearWide, 32, WT>(a, grid, s);
-    if (bk == 64) {
-        if (mode == kModeFused) return launch_tile_t<kModeFused, 64, WT>(a, grid, s);
-        if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64, WT>(a, grid, s);
-        if (mode == kModeLinear) return launch_tile_t<kModeLinear, 64, WT>(a, grid, s);
-        return launch_tile_t<kModePartials, 64, WT>(a, grid, s);
+static hipError_t launch_tile_w(int mode, int bk, int tile, const TileArgs& a, int grid,
+                                hipStream_t s) {
+    if (tile == kTile192) {
+        if (mode == kModeFused) return launch_tile_t<kModeFused, 32, WT, kTile192>(a, grid, s);
+        if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32, WT, kTile192>(a, grid, s);
+        return hipErrorInvalidValue;
     }
-    if (mode == kModeFused) return launch_tile_t<kModeFused, 32, WT>(a, grid, s);
-    if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32, WT>(a, grid, s);
-    if (mode == kModeLinear) return launch_tile_t<kModeLinear, 32, WT>(a, grid, s);
-    return launch_tile_t<kModePartials, 32, WT>(a, grid, s);
+    if (mode == kModeLinearWide) return launch_tile_t<kModeLinearWide, 32, WT, kTile128>(a, grid, s);
+    if (bk == 64) {
+        if (mode == kModeFused) return launch_tile_t<kModeFused, 64, WT, kTile128>(a, grid, s);
+        if (mode == kModeReduced) return launch_tile_t<kModeReduced, 64, WT, kTile128>(a, grid, s);
+        if (mode == kModeLinear) return launch_tile_t<kModeLinear, 64, WT, kTile128>(a, grid, s);
+        return launch_tile_t<kModePartials, 64, WT, kTile128>(a, grid, s);
+    }
+    if (mode == kModeFused) return launch_tile_t<kModeFused, 32, WT, kTile128>(a, grid, s);
+    if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32, WT, kTile128>(a, grid, s);
+    if (mode == kModeLinear) return launch_tile_t<kModeLinear, 32, WT, kTile128>(a, grid, s);
+    return launch_tile_t<kModePartials, 32, WT, kTile128>(a, grid, s);
 }
 
-hipError_t launch_tile(int mode, int bk, bool wt, const TileArgs& a, int grid, hipStream_t s) {
-    return wt ? launch_tile_w<true>(mode, bk, a, grid, s) : launch_tile_w<false>(mode, bk, a, grid, s);
+hipError_t launch_tile(int mode, int bk, bool wt, int tile, const TileArgs& a, int grid,
+                       hipStream_t s) {
+    if (!tile_supported(mode, tile)) return hipErrorInvalidValue;
+    return wt ? launch_tile_w<true>(mode, bk, tile, a, grid, s)
+              : launch_tile_w<false>(mode, bk, tile, a, grid, s);
 }
 
-template <int MODE, int BK>
+template <int MODE, int BK, int TILE>
 static int occ_t() {
-    using C = TileCfg<BK, tile_waves(MODE, BK), tile_bn(MODE)>;
+    using C = typename TileCfgOf<MODE, BK, TILE>::type;
     int n = 0;
-    const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK, false>);
+    const void* fn = reinterpret_cast<const void*>(&tile_kernel<MODE, BK, false, TILE>);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, C::THREADS,
                                                      static_cast<size_t>(C::LDS_BYTES)) != hipSuccess)
         return 0;
     return n;
 }
 
-int tile_occupancy(int mode, int bk) {
-    if (mode == kModeLinearWide) return occ_t<kModeLinearWide, 32>();
+int tile_occupancy(int mode, int bk, int tile) {
+    if (!tile_supported(mode, tile)) return 0;
+    if (tile == kTile192)
+        return mode == kModeFused ? occ_t<kModeFused, 32, kTile192>()
+                                  : occ_t<kModeReduced, 32, kTile192>();
+    if (mode == kModeLinearWide) return occ_t<kModeLinearWide, 32, kTile128>();
     if (bk == 64) {
-        if (mode == kModeFused) return occ_t<kModeFused, 64>();
-        if (mode == kModeReduced) return occ_t<kModeReduced, 64>();
-        if (mode == kModeLinear) return occ_t<kModeLinear, 64>();
-        return occ_t<kModePartials, 64>();
+        if (mode == kModeFused) return occ_t<kModeFused, 64, kTile128>();
+        if (mode == kModeReduced) return occ_t<kModeReduced, 64, kTile128>();
+        if (mode == kModeLinear) return occ_t<kModeLinear, 64, kTile128>();
+        return occ_t<kModePartials, 64, kTile128>();
     }
-    if (mode == kModeFused) return occ_t<kModeFused, 32>();
-    if (mode == kModeReduced) return occ_t<kModeReduced, 32>();
-    if (mode == kModeLinear) return occ_t<kModeLinear, 32>();
-    return occ_t<kModePartials, 32>();
+    if (mode == kModeFused) return occ_t<kModeFused, 32, kTile128>();
+    if (mode == kModeReduced) return occ_t<kModeReduced, 32, kTile128>();
+    if (mode == kModeLinear) return occ_t<kModeLinear, 32, kTile128>();
+    return occ_t<kModePartials, 32, kTile128>();
 }
 
 }  // namespace mmar

@@ -111,6 +111,16 @@ enum {
 
 enum { MMAR_W_AUTO = -1, MMAR_W_DIRECT = 0, MMAR_W_PRETRANSPOSE = 1 };
 
+/* Output tile of the persistent fused kernel (MMAR_SCHED_PERSISTENT, and the head block of
+ * MMAR_SCHED_BALANCED; the chunked schedules always use 256 x 128).
+ *   MMAR_TILE_256x128  8 waves per workgroup, each a 64 x 64 block of the tile.
+ *   MMAR_TILE_256x192  4 waves, each a 128 x 96 block: 42 % fewer operand bytes read from
+ *                      LDS and 22 % fewer bytes copied into it per flop; 3 of a wave's 12
+ *                      running-total blocks are kept in LDS.  K steps of 32.
+ * Both give identical output bits (every 32 x 32 output block sees the same MFMA sequence
+ * and the same reduction and epilogue).  AUTO: the plan's (default 256 x 128). */
+enum { MMAR_TILE_AUTO = -1, MMAR_TILE_256x128 = 0, MMAR_TILE_256x192 = 1 };
+
 /* Activation of the producer MatMul (mmar_linear). */
 enum { MMAR_ACT_NONE = 0, MMAR_ACT_GELU_TANH = 1 };
 
@@ -145,22 +155,24 @@ int mmar_fused_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
 
 /* Workspace bytes a plan needs: K N 2 (256-aligned) for MMAR_W_PRETRANSPOSE, plus the
  * partial-product ring for MMAR_SCHED_SEQUENTIAL (P chunk_m chunk_n 4) and
- * MMAR_SCHED_STREAMS (ring times that).  schedule AUTO: the plan mmar_fused would use
- * (with non-zero chunk / ring and non-AUTO w_mode arguments overriding).  ring = number of
- * chunk slots for MMAR_SCHED_STREAMS (0 = the default, 2).  Returns 0 and sets the last
- * error on invalid arguments. */
+ * MMAR_SCHED_STREAMS (ring times that), plus the tail partials of MMAR_SCHED_BALANCED
+ * (which depend on the tile).  schedule AUTO: the plan mmar_fused would use (with non-zero
+ * chunk / ring and non-AUTO w_mode / tile arguments overriding).  ring = number of chunk
+ * slots for MMAR_SCHED_STREAMS (0 = the default, 2).  Returns 0 and sets the last error on
+ * invalid arguments. */
 size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, int32_t P,
-                            int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode);
+                            int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode,
+                            int32_t tile);
 
-/* The fused block with every choice explicit.  workspace == NULL: the library's
- * workspace is used (serialized per device); otherwise `workspace` (device memory,
- * 16-byte aligned, at least mmar_workspace_bytes(...) bytes, owned by the caller and not
- * used by any other call until the stream passes this one) and the call is re-entrant.
- * A too-small caller workspace returns MMAR_ENOMEM. */
+/* The fused block with every choice explicit (tile: an MMAR_TILE_* value).  workspace ==
+ * NULL: the library's workspace is used (serialized per device); otherwise `workspace`
+ * (device memory, 16-byte aligned, at least mmar_workspace_bytes(...) bytes, owned by the
+ * caller and not used by any other call until the stream passes this one) and the call is
+ * re-entrant.  A too-small caller workspace returns MMAR_ENOMEM. */
 int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
                   int32_t P, float p_drop, uint64_t seed, int32_t schedule, int32_t chunk_m,
-                  int32_t chunk_n, int32_t ring, int32_t w_mode, void* workspace,
+                  int32_t chunk_n, int32_t ring, int32_t w_mode, int32_t tile, void* workspace,
                   size_t ws_bytes, void* stream);
 
 /* MMAR_SCHED_SEQUENTIAL with the library workspace: the comparison point of the CoCoNet
@@ -249,22 +261,25 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
                               int32_t P, float p_drop, uint64_t seed, void* stream);
 
 /* The autotuner (CoCoNet picks its schedules by automatic search; "Key takeaways", first
- * bullet):
- * times candidate {schedule, chunk, ring, weight mode} plans for this shape on library-owned
- * buffers, keeps the fastest in the plan cache (also written to the JSON file named by
- * the MMAR_PLAN_CACHE environment variable, if set) and returns MMAR_OK.  flags: bit 0
- * = also try MMAR_SCHED_STREAMS and MMAR_SCHED_SEQUENTIAL plans.  Synchronizes the
- * device. */
+ * bullet): times candidate {schedule, tile, chunk, weight mode} plans for this shape on
+ * library-owned buffers, 25 rounds interleaved (each round runs every candidate once), and
+ * keeps the default plan unless a candidate's median time beats it by more than the
+ * larger of the two interquartile ranges; the best such candidate goes to the plan cache
+ * (also written, with that margin, to the JSON file named by the MMAR_PLAN_CACHE
+ * environment variable, if set).  flags: bit 0 = also try MMAR_SCHED_STREAMS and
+ * MMAR_SCHED_SEQUENTIAL plans.  Synchronizes the device. */
 int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags);
 
 /* Set / read the plan used by mmar_fused for this shape on the current device.
- * schedule is one of MMAR_SCHED_*, AUTO clears the entry; w_mode one of MMAR_W_*.
- * mmar_get_plan writes the plan that mmar_fused would use (the default when none is
- * set: persistent, whole-output chunk, MMAR_W_DIRECT). */
+ * schedule is one of MMAR_SCHED_*, AUTO clears the entry; w_mode one of MMAR_W_*; tile
+ * one of MMAR_TILE_*.  mmar_get_plan writes the plan that mmar_fused would use (the
+ * default when none is set: persistent, whole-output chunk, MMAR_W_DIRECT,
+ * MMAR_TILE_256x128). */
 int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
-                  int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode);
+                  int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode, int32_t tile);
 int mmar_get_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t* schedule,
-                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring, int32_t* w_mode);
+                  int32_t* chunk_m, int32_t* chunk_n, int32_t* ring, int32_t* w_mode,
+                  int32_t* tile);
 
 /* Text of the last error on the calling thread ("" if none).  Valid until the next
  * call on this thread. */

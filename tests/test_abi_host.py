@@ -56,12 +56,15 @@ def test_other_entry_points_validate():
     assert L.mmar_reduce_epilogue_only(FAKE, FAKE, FAKE, FAKE, 64, 64, 2, 2.0, 0, None) == mmar.EINVAL
     assert L.mmar_reduce_epilogue_only(FAKE, FAKE, FAKE, FAKE, 60, 64, 2, 0.1, 0, None) == mmar.EINVAL
     assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 7,
-                           0, 0, 0, -1, None, 0, None) == mmar.EINVAL
+                           0, 0, 0, -1, -1, None, 0, None) == mmar.EINVAL
     assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 2,
-                           0, 0, 9, -1, None, 0, None) == mmar.EINVAL
+                           0, 0, 9, -1, -1, None, 0, None) == mmar.EINVAL
     assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 2,
-                           0, 0, 0, 5, None, 0, None) == mmar.EINVAL
+                           0, 0, 0, 5, -1, None, 0, None) == mmar.EINVAL
     assert "weight mode" in mmar.last_error()
+    assert L.mmar_fused_ex(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 256, 4, 0.1, 0, 3,
+                           0, 0, 0, -1, 2, None, 0, None) == mmar.EINVAL
+    assert "tile" in mmar.last_error()
     assert L.mmar_fused_nt(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, FAKE * 64, 64, 256, 250, 4, 0.1, 0, 0,
                            0, None) == mmar.EINVAL
     assert L.mmar_transpose_weight(FAKE, FAKE, 64, 64, None) == mmar.EINVAL   # overlap
@@ -101,7 +104,8 @@ def test_other_entry_points_validate():
     assert L.mmar_linear(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 64, 250, 0, None) == mmar.EINVAL
     assert L.mmar_linear(FAKE, FAKE * 2, FAKE * 3, FAKE * 4, 64, 64, 256, 7, None) == mmar.EINVAL
     assert b"activation" in L.mmar_last_error()
-    assert L.mmar_set_plan(64, 256, 256, 4, 9, 0, 0, 0, -1) == mmar.EINVAL
+    assert L.mmar_set_plan(64, 256, 256, 4, 9, 0, 0, 0, -1, -1) == mmar.EINVAL
+    assert L.mmar_set_plan(64, 256, 256, 4, 3, 0, 0, 0, -1, 7) == mmar.EINVAL
     assert L.mmar_autotune(64, 256, 250, 4, 0) == mmar.EINVAL
 
 
@@ -117,8 +121,14 @@ def test_balanced_schedule_workspace_and_chunk():
     with pytest.raises(mmar.MmarError):
         mmar.workspace_bytes("balanced", 8192, 2560, 10240, 8, chunk=(4096, 0))
     L = mmar.lib
-    assert L.mmar_set_plan(8192, 2560, 10240, 8, 4, 4096, 0, 0, -1) == mmar.EINVAL
-    assert L.mmar_workspace_bytes(5, 8192, 2560, 10240, 8, 0, 0, 0, -1) == 0
+    assert L.mmar_set_plan(8192, 2560, 10240, 8, 4, 4096, 0, 0, -1, -1) == mmar.EINVAL
+    assert L.mmar_workspace_bytes(5, 8192, 2560, 10240, 8, 0, 0, 0, -1, -1) == 0
+    # with 256 x 192 tiles: 32 x 14 = 448 tiles; the head is 8192 x 1536 (256 tiles), the
+    # tail 8192 x 1024
+    assert mmar.workspace_bytes("balanced", 8192, 2560, 10240, 8, tile="256x192") == 8 * 8192 * 1024 * 4
+    # 8192 x 3072 on 256 x 192 tiles is 512 tiles: two full rounds, no tail
+    assert mmar.workspace_bytes("balanced", 8192, 3072, 12288, 16, tile="256x192") == 0
+    assert L.mmar_workspace_bytes(4, 8192, 2560, 10240, 8, 0, 0, 0, -1, 3) == 0
 
 
 def test_workspace_bytes():

@@ -22,30 +22,34 @@ import chunked_matmul_reduce_amd as mmar  # noqa: E402
 
 ONE = 0x3F80
 SCHEDS = ["persistent", "sequential", "streams", "balanced"]   # balanced: whole-output chunk only
+# (schedule, tile): the persistent kernel and the balanced schedule's head on both tile
+# shapes; the chunked schedules have one
+PLANS = [("persistent", "256x128"), ("persistent", "256x192"), ("sequential", "auto"),
+         ("streams", "auto"), ("balanced", "256x128"), ("balanced", "256x192")]
 
 
 def _to_dev(inp):
     return {k: dev(inp[k], torch) for k in ("X", "W", "bias", "residual")}
 
 
-def _run(d, P, p, seed, sched="auto", chunk=(0, 0), ring=0, w_mode="auto"):
-    if sched == "auto" and w_mode == "auto":
+def _run(d, P, p, seed, sched="auto", chunk=(0, 0), ring=0, w_mode="auto", tile="auto"):
+    if sched == "auto" and w_mode == "auto" and tile == "auto":
         out = mmar.fused(d["X"], d["W"], d["bias"], d["residual"], P, p, seed, chunk=chunk)
     else:
         out = mmar.fused_ex(d["X"], d["W"], d["bias"], d["residual"], P, p, seed, sched,
-                            chunk=chunk, ring=ring, w_mode=w_mode)
+                            chunk=chunk, ring=ring, w_mode=w_mode, tile=tile)
     torch.cuda.synchronize()
     return host(out)
 
 
-def _mask_readout(M, N, K, P, p, seed, sched="auto", chunk=(0, 0)):
+def _mask_readout(M, N, K, P, p, seed, sched="auto", chunk=(0, 0), tile="auto"):
     """X = 0, bias = 1, residual = 0: out is exactly 0 (dropped) or scale (kept)."""
     X = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
     W = torch.zeros((K, N), dtype=torch.bfloat16, device="cuda")
     b = torch.ones((N,), dtype=torch.bfloat16, device="cuda")
     r = torch.zeros((M, N), dtype=torch.bfloat16, device="cuda")
     d = {"X": X, "W": W, "bias": b, "residual": r}
-    out = _run(d, P, p, seed, sched, chunk)
+    out = _run(d, P, p, seed, sched, chunk, tile=tile)
     scale = np.float32(1.0 / (1.0 - float(np.float32(p))))
     assert np.all((out == 0) | (out == scale))
     return out != 0
@@ -68,15 +72,15 @@ def test_tiny_all_schedules_chunks_bit_identical():
     inp = make_inputs("tiny")
     d = _to_dev(inp)
     outs = {}
-    for sched in SCHEDS:
+    for sched, tile in PLANS:
         for chunk in [(32, 64), (64, 64), (32, 256), (64, 256), (0, 0)]:
             if sched == "balanced" and chunk != (0, 0):
                 continue
             for wm in ("direct", "pretranspose"):
-                out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, w_mode=wm)
-                outs[(sched, chunk, wm)] = out
-                print(sched, chunk, wm, "max rel err", _check_block(inp, out), flush=True)
-    ref = f32_bits(outs[("persistent", (32, 64), "direct")])
+                out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, w_mode=wm, tile=tile)
+                outs[(sched, tile, chunk, wm)] = out
+                print(sched, tile, chunk, wm, "max rel err", _check_block(inp, out), flush=True)
+    ref = f32_bits(outs[("persistent", "256x128", (32, 64), "direct")])
     for k, o in outs.items():
         assert np.array_equal(f32_bits(o), ref), k
     keep = _mask_readout(w.M, w.N, w.K, w.P, inp["p_drop"], w.seed, chunk=w.chunk)
@@ -106,16 +110,17 @@ def test_ragged_shapes_against_oracle(M, K, N, P):
     inp.update(M=M, K=K, N=N, P=P, p_drop=np.float32(0.2), seed=(M << 40) + N)
     d = _to_dev(inp)
     ref = None
-    for sched in SCHEDS:
+    print("ragged", M, K, N, P, flush=True)
+    for sched, tile in PLANS:
         for chunk in [(0, 0), (32, 32), (M // 2 if (M // 2) % 32 == 0 else M, N)]:
             if sched == "balanced" and chunk != (0, 0):
                 continue
             for wm in ("direct", "pretranspose"):
-                out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk, w_mode=wm)
+                out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk, w_mode=wm, tile=tile)
                 _check_block(inp, out)
                 if ref is None:
                     ref = f32_bits(out)
-                assert np.array_equal(f32_bits(out), ref), (sched, chunk, wm)
+                assert np.array_equal(f32_bits(out), ref), (sched, tile, chunk, wm)
     # the weight given transposed (Linear layout)
     Wt = mmar.transpose_weight(d["W"])
     torch.cuda.synchronize()
@@ -126,28 +131,53 @@ def test_ragged_shapes_against_oracle(M, K, N, P):
 
 
 # ---------------------------------------------------------------- full-size workloads
-def _sample_rows(M, rng):
-    edge = [0, 1, 31, 32, 63, 64, 255, 256, M // 2, M - 257, M - 256, M - 1]
-    return np.unique(np.concatenate([np.array(edge), rng.choice(M, size=180, replace=False)]))
-
-
 @pytest.mark.parametrize("name", ["gpt2_attn", "gpt2_mlp", "bert_mlp", "gpt3_mlp"])
 def test_full_size_workload(name):
-    """The launch configuration the benchmark times (library plan, default chunk)."""
+    """The launch configuration the benchmark times (library plan, default chunk) and the
+    persistent kernel on the other tile shape: bit-identical to each other, every output
+    element against the oracle (all M rows), the dropout mask bit for bit."""
     w = WORKLOADS[name]
     inp = make_inputs(name)
     d = _to_dev(inp)
+    print(name, "GPU runs", flush=True)
     out = _run(d, w.P, inp["p_drop"], w.seed)
-    rows = _sample_rows(w.M, np.random.default_rng(w.seed))
-    worst = _check_block(inp, out, rows=rows)
-    keep = oracle.keep_mask(w.M, w.N, inp["p_drop"], w.seed)
-    res32 = (inp["residual"].astype(np.uint32) << 16).view(np.float32)
-    assert np.array_equal(f32_bits(out[~keep]), f32_bits(res32[~keep]))
+    plan_tile = mmar.get_plan(w.M, w.N, w.K, w.P)["tile"]
+    other = "256x192" if plan_tile == mmar.TILE_256x128 else "256x128"
+    out2 = _run(d, w.P, inp["p_drop"], w.seed, "persistent", tile=other)
+    assert np.array_equal(f32_bits(out), f32_bits(out2)), other
+    del out2
+    print(name, "oracle over all rows", flush=True)
+    worst = _check_block(inp, out)
     del d
     torch.cuda.empty_cache()
-    gkeep = _mask_readout(w.M, w.N, w.K, w.P, inp["p_drop"], w.seed)
-    assert np.array_equal(gkeep, keep)
-    print(name, "max rel err on sampled rows", worst, "kept", keep.mean(), flush=True)
+    keep = oracle.keep_mask(w.M, w.N, inp["p_drop"], w.seed)
+    for tile in ("256x128", "256x192"):
+        gkeep = _mask_readout(w.M, w.N, w.K, w.P, inp["p_drop"], w.seed, sched="persistent",
+                              tile=tile)
+        assert np.array_equal(gkeep, keep), tile
+    print(name, "max rel err over all rows", worst, "kept", keep.mean(), flush=True)
+
+
+def test_threshold_tie_is_kept_on_gpu():
+    """A Philox word equal to floor(p * 2^32) keeps its element (drop iff r < threshold,
+    strictly), on every schedule and tile: p is chosen so that the threshold equals the
+    word of one element exactly; one ulp more of p drops that element."""
+    import oracle.philox as philox
+    M, N, K, P = 64, 256, 256, 4
+    for seed in range(100000):
+        r = philox.block_scalar((0, 0, 0, 0), (seed, 0))[0]   # element 0's word
+        if r % 256 == 0 and r > 2 ** 24:
+            break
+    p = np.float32(r / 2 ** 32)
+    assert oracle.drop_threshold(p) == r
+    p_up = np.nextafter(p, np.float32(1))
+    for sched, tile in PLANS:
+        keep = _mask_readout(M, N, K, P, p, seed, sched=sched, tile=tile)
+        assert keep[0, 0], (sched, tile)
+        assert np.array_equal(keep, oracle.keep_mask(M, N, p, seed)), (sched, tile)
+        keep_up = _mask_readout(M, N, K, P, p_up, seed, sched=sched, tile=tile)
+        assert not keep_up[0, 0], (sched, tile)
+        assert np.array_equal(keep_up, oracle.keep_mask(M, N, p_up, seed)), (sched, tile)
 
 
 def test_full_size_schedule_invariance():
@@ -155,14 +185,17 @@ def test_full_size_schedule_invariance():
     inp = make_inputs("gpt2_attn")
     d = _to_dev(inp)
     ref = f32_bits(_run(d, w.P, inp["p_drop"], w.seed, "persistent", w_mode="direct"))
-    for sched, chunk, ring, wm in [("persistent", (0, 0), 0, "pretranspose"),
-                                   ("persistent", (w.M // 2, w.N // 2), 0, "direct"),
-                                   ("persistent", (1024, 3072), 0, "pretranspose"),
-                                   ("streams", (1024, w.N), 2, "direct"),
-                                   ("streams", (2048, 1536), 3, "pretranspose"),
-                                   ("sequential", (0, 0), 0, "direct")]:
-        out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, ring, w_mode=wm)
-        assert np.array_equal(f32_bits(out), ref), (sched, chunk, ring, wm)
+    for sched, chunk, ring, wm, tile in [("persistent", (0, 0), 0, "pretranspose", "256x128"),
+                                         ("persistent", (w.M // 2, w.N // 2), 0, "direct", "256x128"),
+                                         ("persistent", (1024, 3072), 0, "pretranspose", "256x128"),
+                                         ("persistent", (0, 0), 0, "pretranspose", "256x192"),
+                                         ("persistent", (2048, 1536), 0, "direct", "256x192"),
+                                         ("persistent", (1024, 3072), 0, "direct", "256x192"),
+                                         ("streams", (1024, w.N), 2, "direct", "auto"),
+                                         ("streams", (2048, 1536), 3, "pretranspose", "auto"),
+                                         ("sequential", (0, 0), 0, "direct", "auto")]:
+        out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, ring, w_mode=wm, tile=tile)
+        assert np.array_equal(f32_bits(out), ref), (sched, chunk, ring, wm, tile)
 
 
 # (M, K, N, P) with a head of whole rounds on 256 CUs and a tail: one ragged tile column,
@@ -182,8 +215,9 @@ def test_balanced_split_bits_and_oracle(M, K, N, P):
     d = _to_dev(inp)
     ref = _run(d, P, inp["p_drop"], inp["seed"], "persistent", w_mode="direct")
     for wm in ("direct", "pretranspose"):
-        out = _run(d, P, inp["p_drop"], inp["seed"], "balanced", w_mode=wm)
-        assert np.array_equal(f32_bits(out), f32_bits(ref)), wm
+        for tile in ("256x128", "256x192"):
+            out = _run(d, P, inp["p_drop"], inp["seed"], "balanced", w_mode=wm, tile=tile)
+            assert np.array_equal(f32_bits(out), f32_bits(ref)), (wm, tile)
     rng = np.random.default_rng(M + N)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 33, M - 32, M - 1],
                                      rng.choice(M, 40, replace=False)]))
@@ -223,19 +257,30 @@ def _golden():
         return json.load(f)
 
 
-@pytest.mark.parametrize("sched", SCHEDS)
-def test_per_slice_accumulation_exact(sched):
+@pytest.mark.parametrize("sched,tile", PLANS)
+def test_per_slice_accumulation_exact(sched, tile):
     g = _golden()["per_slice_2p24"]
     inp = _struct_inputs(2, 64, ["big", "unit_per_32"])
-    out = _run(_to_dev(inp), 2, 0.0, 0, sched)
+    out = _run(_to_dev(inp), 2, 0.0, 0, sched, tile=tile)
     assert np.all(out == np.float32(g["per_slice_fp32"]))
 
 
-@pytest.mark.parametrize("sched", SCHEDS)
-def test_slice_order_exact(sched):
+@pytest.mark.parametrize("sched,tile", PLANS)
+def test_slice_order_exact(sched, tile):
     g = _golden()["slice_order"]
     inp = _struct_inputs(3, 64, ["big", "one", "-big"])
-    out = _run(_to_dev(inp), 3, 0.0, 0, sched)
+    out = _run(_to_dev(inp), 3, 0.0, 0, sched, tile=tile)
+    assert np.all(out == np.float32(g["left_to_right_fp32"]))
+
+
+@pytest.mark.parametrize("tile", ["256x128", "256x192"])
+def test_slice_order_exact_many_slices(tile):
+    """The slice-order pin with the running total carried over many slices (P = 16, the
+    GPT-2 blocks' slice count): S_0 = 2^24, S_1 = 1, S_2 = -2^24, then 13 zero slices;
+    left to right gives 0 exactly.  M and N span several tiles of either shape."""
+    g = _golden()["slice_order"]
+    inp = _struct_inputs(16, 64, ["big", "one", "-big"] + ["zero"] * 13, M=512, N=384)
+    out = _run(_to_dev(inp), 16, 0.0, 0, "persistent", tile=tile)
     assert np.all(out == np.float32(g["left_to_right_fp32"]))
 
 
@@ -243,9 +288,9 @@ def test_p_one_is_residual_bits():
     inp = make_random_inputs(256, 512, 384, seed=11)
     d = _to_dev(inp)
     res32 = (inp["residual"].astype(np.uint32) << 16).view(np.float32)
-    for sched in SCHEDS:
-        out = _run(d, 4, 1.0, 5, sched)
-        assert np.array_equal(f32_bits(out), f32_bits(res32))
+    for sched, tile in PLANS:
+        out = _run(d, 4, 1.0, 5, sched, tile=tile)
+        assert np.array_equal(f32_bits(out), f32_bits(res32)), (sched, tile)
 
 
 @pytest.mark.parametrize("p", [0.0, 0.1, 0.3])
@@ -257,18 +302,22 @@ def test_epilogue_closed_form_bits(p):
     keep = oracle.keep_mask(M, N, p, 77)
     want = oracle.reduce_epilogue_fp32([np.zeros((M, N))], inp["bias"], inp["residual"], keep, p)
     d = _to_dev(inp)
-    for sched in SCHEDS:
-        out = _run(d, P, p, 77, sched)
-        assert np.array_equal(f32_bits(out), f32_bits(want)), sched
+    for sched, tile in PLANS:
+        out = _run(d, P, p, 77, sched, tile=tile)
+        assert np.array_equal(f32_bits(out), f32_bits(want)), (sched, tile)
 
 
 # ---------------------------------------------------------------- measurement entry points
-def test_gemm_only_and_partials_compose_to_fused():
+@pytest.mark.parametrize("tile", ["256x128", "256x192"])
+def test_gemm_only_and_partials_compose_to_fused(tile):
     M, K, N, P = 512, 1024, 384, 4
     inp = make_random_inputs(M, K, N, seed=13)
     d = _to_dev(inp)
     fused = _run(d, P, 0.1, 3, "persistent", w_mode="direct")
+    mmar.set_plan(M, N, K, P, "persistent", tile=tile)   # gemm_only runs the plan's tile
+    assert mmar.get_plan(M, N, K, P)["tile"] == mmar.TILES[tile]
     T = mmar.gemm_only(d["X"], d["W"], P)
+    mmar.set_plan(M, N, K, P, "auto")
     o1 = mmar.reduce_epilogue_only(T[None], d["bias"], d["residual"], 0.1, 3)
     parts = mmar.gemm_partials(d["X"], d["W"], P)
     o2 = mmar.reduce_epilogue_only(parts, d["bias"], d["residual"], 0.1, 3)
@@ -321,7 +370,7 @@ def test_invalid_arguments_leave_out_untouched():
     assert rc == mmar.EALIGN
     small = torch.empty(16, dtype=torch.uint8, device="cuda")
     rc = mmar.lib.mmar_fused_ex(*ptrs, out.data_ptr(), M, N, K, P, 0.1, 1, mmar.SCHED_SEQUENTIAL,
-                                0, 0, 0, mmar.W_DIRECT, small.data_ptr(), 16, None)
+                                0, 0, 0, mmar.W_DIRECT, mmar.TILE_AUTO, small.data_ptr(), 16, None)
     assert rc == mmar.ENOMEM
     torch.cuda.synchronize()
     assert torch.all(out == 7.0)
@@ -349,7 +398,7 @@ def test_full_size_tuned_plan(name):
     """The configuration the benchmark times: the plan mmar_autotune picks for the
     workload (after warm-up calls, as the benchmark does), bit-identical to the default
     plan; for the benchmark's own workload, the tuned call on its seeded inputs against
-    the oracle on sampled rows and the dropped elements."""
+    the oracle on every output element and the dropped elements."""
     w = WORKLOADS[name]
     M, K, N, P = w.M, w.K, w.N, w.P
     print("tuned plan", name, flush=True)
@@ -375,8 +424,7 @@ def test_full_size_tuned_plan(name):
         out = _run(d, P, p, seed)
         assert np.array_equal(f32_bits(out), ref), plan
         if name == "gpt2_mlp":
-            rows = _sample_rows(M, np.random.default_rng(w.seed + 1))
-            _check_block(inp, out, rows=rows)
+            _check_block(inp, out)   # every output element
     finally:
         mmar.set_plan(M, N, K, P, "auto")
 
