@@ -61,6 +61,9 @@ _SIGNATURES = {
     "mmar_get_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                      ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                      ctypes.POINTER(_I32)]),
+    "mmar_fused_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32,
+                                          _I32, _I32, _I32, _I32, _I32, _P]),
+    "mmar_noalloc_workspace_capacity": (_SZ, []),
     "mmar_last_error": (ctypes.c_char_p, []),
     "mmar_version": (ctypes.c_char_p, []),
     "mmar_release": (ctypes.c_int, []),
@@ -232,6 +235,35 @@ def fused_ex(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0), ring
                                _stream(X.device, stream))
     _check(rc)
     return out
+
+
+def fused_noalloc(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0), ring=0,
+                  w_mode="auto", tile="auto", out=None, stream=None):
+    """mmar_fused_noalloc: fused_ex with the library's static per-device workspace
+    (``noalloc_workspace_capacity()`` bytes), for callers that cannot allocate; ``out`` must
+    be given by such callers (None allocates it here, for convenience in tests)."""
+    torch = _torch()
+    if isinstance(schedule, str):
+        schedule = SCHEDULES[schedule]
+    if isinstance(w_mode, str):
+        w_mode = W_MODES[w_mode]
+    if isinstance(tile, str):
+        tile = TILES[tile]
+    M, N, K = _shapes(X, W, P)
+    out = _out(out, (M, N), X)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_fused_noalloc(_bits(X, "X", (M, K)), _bits(W, "W", (K, N)),
+                                    _bits(bias, "bias", (N,)), _bits(residual, "residual", (M, N)),
+                                    out.data_ptr(), M, N, K, int(P), float(p_drop),
+                                    int(seed) & (2 ** 64 - 1), int(schedule), int(chunk[0]),
+                                    int(chunk[1]), int(ring), int(w_mode), int(tile),
+                                    _stream(X.device, stream))
+    _check(rc)
+    return out
+
+
+def noalloc_workspace_capacity() -> int:
+    return int(lib.mmar_noalloc_workspace_capacity())
 
 
 def fused_nt(X, Wt, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, stream=None):

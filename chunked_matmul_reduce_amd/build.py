@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmmar.so")
 SOURCES = [os.path.join(PKG, "csrc", "tile_kernel.hip"), os.path.join(PKG, "csrc", "reduce_kernels.hip"),
            os.path.join(PKG, "csrc", "unfused.hip"), os.path.join(PKG, "csrc", "adam.hip"),
-           os.path.join(PKG, "csrc", "mmar.cpp")]
+           os.path.join(PKG, "csrc", "noalloc.hip"), os.path.join(PKG, "csrc", "mmar.cpp")]
 HEADERS = [os.path.join(PKG, "csrc", "mmar_internal.h"), os.path.join(PKG, "csrc", "device_common.h"),
            os.path.join(ROOT, "include", "mmar.h")]
 ARCH = "gfx950"

@@ -718,6 +718,49 @@ int fused_impl(const uint16_t* X, const uint16_t* W, bool w_t, const uint16_t* b
     return run_plan(st, c, p, kRunFused, workspace, ws_bytes, static_cast<hipStream_t>(stream));
 }
 
+}  // namespace
+
+namespace mmar {
+
+void set_error(const char* msg) { g_err = msg; }
+
+// The fused block with a workspace of fixed capacity that the caller provides (no
+// allocation anywhere on this path): the plan is resolved as for mmar_fused_ex; a plan
+// needing the side stream (MMAR_SCHED_STREAMS, whose stream and events are created on
+// first use) or more than ws_cap bytes is rejected before any device work.
+int fused_fixed_ws(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                   const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                   int32_t P, float p_drop, uint64_t seed, int32_t sched, int32_t chunk_m,
+                   int32_t chunk_n, int32_t ring, int32_t wmode, int32_t tile, void* ws,
+                   size_t ws_cap, void* stream) {
+    g_err.clear();
+    Call c;
+    const Shape s{M, N, K, P};
+    int rc = check_call(X, W, bias, residual, out, s, p_drop, seed, chunk_m, chunk_n, &c);
+    if (rc) return rc;
+    if ((rc = check_sched(sched, ring, wmode, tile))) return rc;
+    if (sched == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
+        return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    const Plan p = plan_for(st, s, sched, chunk_m, chunk_n, ring, wmode, tile);
+    if (p.sched == MMAR_SCHED_STREAMS)
+        return fail(MMAR_EINVAL,
+                    "the streams schedule needs the library's side stream; not available without "
+                    "allocation");
+    const size_t need = ws_bytes_for(s, p, false);
+    if (need > ws_cap)
+        return fail(MMAR_ENOMEM, "the plan needs " + std::to_string(need) +
+                                     " bytes of workspace; the static workspace holds " +
+                                     std::to_string(ws_cap));
+    return run_with_ws(st, c, p, kRunFused, static_cast<char*>(ws),
+                       static_cast<hipStream_t>(stream));
+}
+
+}  // namespace mmar
+
+namespace {
+
 // ------------------------------------------------------------------ autotuner
 // Median and interquartile range of a sorted sample.
 void med_iqr(std::vector<float> t, float* med, float* iqr) {

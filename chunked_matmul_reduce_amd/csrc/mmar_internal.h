@@ -115,6 +115,16 @@ hipError_t launch_adam(const AdamArgs& a, int grid, hipStream_t s);
 hipError_t launch_unfused_tail(const float* ws, float* T, const uint16_t* bias,
                                const uint16_t* residual, float* out, uint8_t* mask, int64_t M,
                                int64_t N, int32_t P, const DropParams& d, int grid, hipStream_t s);
+// Host-side entry for callers that bring a fixed workspace and must not allocate
+// (mmar.cpp): the fused block with the plan resolved as for mmar_fused_ex; MMAR_* codes.
+int fused_fixed_ws(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                   const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                   int32_t P, float p_drop, uint64_t seed, int32_t sched, int32_t chunk_m,
+                   int32_t chunk_n, int32_t ring, int32_t wmode, int32_t tile, void* ws,
+                   size_t ws_cap, void* stream);
+// Sets the calling thread's last-error text (mmar_last_error).
+void set_error(const char* msg);
+
 // Workgroups of the tile kernel that fit on one CU at once (0 on error or for a shape
 // the mode does not have).
 int tile_occupancy(int mode, int bk, int tile);

@@ -175,6 +175,22 @@ int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   int32_t chunk_n, int32_t ring, int32_t w_mode, int32_t tile, void* workspace,
                   size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): mmar_fused_ex with its workspace taken
+ * from a static per-device array of mmar_noalloc_workspace_capacity() bytes (64 MiB) that
+ * the library holds from load to process exit; no hipMalloc, hipFree or other allocation
+ * on this path.  Arguments as mmar_fused_ex (without workspace); the plan is resolved the
+ * same way.  Plans whose workspace exceeds the capacity return MMAR_ENOMEM, and
+ * MMAR_SCHED_STREAMS (whose side stream and events are created on first use) returns
+ * MMAR_EINVAL, both before any device work.  Every call on a device shares that device's
+ * array: calls that overlap on one device (two streams, two threads) race. */
+int mmar_fused_noalloc(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
+                       const uint16_t* residual, float* out, int64_t M, int64_t N, int64_t K,
+                       int32_t P, float p_drop, uint64_t seed, int32_t schedule,
+                       int32_t chunk_m, int32_t chunk_n, int32_t ring, int32_t w_mode,
+                       int32_t tile, void* stream);
+size_t mmar_noalloc_workspace_capacity(void);
+
 /* MMAR_SCHED_SEQUENTIAL with the library workspace: the comparison point of the CoCoNet
  * record that fuses the same work but does not overlap it ("Key takeaways", second
  * bullet). */
