@@ -193,6 +193,13 @@ __device__ __forceinline__ void dma16x1(const void* sbase, uint32_t voff, uint32
         : "memory");
 }
 
+// Byte bias a copy's per-lane source offset carries against its instruction offset: +1 KB
+// for the first copy of a pair.
+template <int TILE, int NQ>
+__device__ __forceinline__ uint32_t copy_bias(int q) {
+    return (q % 2 == 0 && q + 1 < NQ) ? 1024u : 0u;
+}
+
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
@@ -289,7 +296,7 @@ void tile_kernel(TileArgs a) {
             const int r = idx / C::CPR, pos = idx % C::CPR;
             const int c = pos ^ swz_x<BK>(r);
             xoff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * a.K + 8 * c) * 2 +
-                                            (q % 2 == 0 ? 1024 : 0));
+                                            copy_bias<TILE, C::XQ>(q));
         }
 #pragma unroll
         for (int q = 0; q < C::WQ; ++q) {
@@ -299,13 +306,13 @@ void tile_kernel(TileArgs a) {
                 const int c = pos ^ swz_x<BK>(r);
                 woff[q] = static_cast<uint32_t>(
                     (static_cast<int64_t>(min(r, cols - 1)) * a.K + 8 * c) * 2 +
-                    (q % 2 == 0 && q + 1 < C::WQ ? 1024 : 0));
+                    copy_bias<TILE, C::WQ>(q));
             } else {
                 const int k = idx / (BN / 8), pos = idx % (BN / 8);
                 const int c = pos ^ swz_w<BN>(k);
                 woff[q] = static_cast<uint32_t>(
                     (static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2 +
-                    (q % 2 == 0 && q + 1 < C::WQ ? 1024 : 0));
+                    copy_bias<TILE, C::WQ>(q));
             }
         }
         const int nsteps = (p_hi - p_lo) * sps;
@@ -422,48 +429,66 @@ void tile_kernel(TileArgs a) {
             // at the start of a k step.  All copies of step st + LEAD go between the MFMAs
             // of the first k step, the handshake before the second.
             static_assert(KS == 2, "the 256 x 192 tile steps K by 32");
-            bf16x8 xf[MB], wf0[NB], wf1[NB];
+            static_assert(C::XQ == 4 && C::WQ == 3, "copy groups of the 256 x 192 tile");
+            // Fragments double-buffered: buffer 0 holds k step 0 of a K step, buffer 1 k
+            // step 1; each k step starts by reading the other buffer's fragments, so the
+            // reads of a stage are all issued a whole k step before the handshake waits
+            // for them.
+            bf16x8 xf0[MB], wf0[NB], xf1[MB], wf1[NB];
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) xf[mb] = read_x(0, 0, mb);
+            for (int mb = 0; mb < MB; ++mb) xf0[mb] = read_x(0, 0, mb);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) wf0[nb] = read_w(0, 0, nb);
-
+            // One K step as two k steps of 12 MFMA slots each (mb outer, nb inner).  A single
+            // wave per SIMD issues in order, so each slot holds one MFMA and at most a few
+            // other instructions, which then issue while the MFMA runs: in k step 0 the
+            // fragment reads for k step 1 (W first, then X in MFMA order), then the X and W
+            // copies of step st + LEAD, then the handshake in the last slot (by then the
+            // reads it waits for have long returned); in k step 1 the reads of the next K
+            // step's first fragments.
             auto kstep192 = [&](auto zero_tag) {
                 constexpr bool ZERO = decltype(zero_tag)::value;
                 const int st2 = min(st + C::LEAD, last);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) wf1[nb] = read_w(st, 1, nb);
-                int c = 0;
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            wf0[nb], xf[mb], ZERO ? f32x16{} : S[nb][mb], 0, 0, 0);
-                        const int upto = ((mb * NB + nb + 1) * C::OPS + NB * MB - 1) / (NB * MB);
-                        while (c < upto) {
-                            __builtin_amdgcn_sched_barrier(0);
-                            copy_op(st2, c);
-                            c += 1;
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                    }
-                    xf[mb] = read_x(st, 1, mb);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                handshake();
                 const int nx = min(st + 1, last);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) wf0[nb] = read_w(nx, 0, nb);
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb)
-                        S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf1[nb], xf[mb],
-                                                                            S[nb][mb], 0, 0, 0);
-                    xf[mb] = read_x(nx, 0, mb);
+                // copy sources and LDS destinations of step st2, computed in slots 3 and 4,
+                // used by the four copy operations in slots 7-10 (X pair, X pair, W pair,
+                // W single)
+                const uint16_t* xsrc = nullptr;
+                const uint16_t* wsrc = nullptr;
+                uint32_t xdst = 0, wdst = 0;
+                static_for<0, MB * NB>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value, mb = i / NB, nb = i % NB;
+                    S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        wf0[nb], xf0[mb], ZERO ? f32x16{} : S[nb][mb], 0, 0, 0);
+                    if constexpr (i < NB) wf1[i] = read_w(st, 1, i);
+                    else if constexpr (i < NB + MB) xf1[i - NB] = read_x(st, 1, i - NB);
+                    if constexpr (i == 3) {
+                        xsrc = step_ptr(xbase, st2, xstep_b);
+                        xdst = lds_addr(xs_base + xstage(st2) * C::XS + C::XQ * uwave * 512);
+                    } else if constexpr (i == 4) {
+                        wsrc = step_ptr(wbase, st2, wstep_b);
+                        wdst = lds_addr(ws_base + wstage(st2) * C::WS + C::WQ * uwave * 512);
+                    } else if constexpr (i == 7) {
+                        dma16x2(xsrc, xoff[0], xoff[1], xdst + 1024);
+                    } else if constexpr (i == 8) {
+                        dma16x2(xsrc, xoff[2], xoff[3], xdst + 3072);
+                    } else if constexpr (i == 9) {
+                        dma16x2(wsrc, woff[0], woff[1], wdst + 1024);
+                    } else if constexpr (i == 10) {
+                        dma16x1(wsrc, woff[2], wdst + 2048);
+                    } else if constexpr (i == MB * NB - 1) {
+                        handshake();
+                    }
                     __builtin_amdgcn_sched_barrier(0);
-                }
+                });
+                static_for<0, MB * NB>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value, mb = i / NB, nb = i % NB;
+                    S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf1[nb], xf1[mb],
+                                                                        S[nb][mb], 0, 0, 0);
+                    if constexpr (i < NB) wf0[i] = read_w(nx, 0, i);
+                    else if constexpr (i < NB + MB) xf0[i - NB] = read_x(nx, 0, i - NB);
+                    __builtin_amdgcn_sched_barrier(0);
+                });
             };
 
             // T = 0 + S_0 after the first slice, then T + S_1, T + S_2, ... (fp32, nearest
