@@ -34,6 +34,8 @@ its first launches; the timed steps then run at the sustained clock.
 --only producer  time only the producer MatMuls (the GeLU layer of the workload's MLP and
                  the GPT-2 QKV projection), for their kernel traces
 --only copy      one plain 1 GiB device copy, the calibration point for HBM counters
+--only vendor    time only hipBLASLt's plain bf16 GEMM at the block's shape (torch.matmul),
+                 the vendor yardstick, for its kernel trace
 """
 import argparse
 import hashlib
@@ -48,6 +50,24 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "fused GEMM+reduce+epilogue TFLOP/s, % bf16 MFMA peak, % epilogue hidden"
+
+
+def _paired(torch, fa, fb, pairs):
+    """Runs fa, fb alternately (ABAB...) ``pairs`` times, each launch between HIP events on
+    the current stream, so both see the same clock and cache state.  Returns the medians
+    of a and b and the median and interquartile range of the per-pair differences a - b
+    (ms)."""
+    s = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(pairs)]
+    for e in ev:
+        e[0].record(s); fa(); e[1].record(s)
+        e[2].record(s); fb(); e[3].record(s)
+    torch.cuda.synchronize()
+    ta = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    tb = sorted(e[2].elapsed_time(e[3]) for e in ev)
+    d = sorted(e[0].elapsed_time(e[1]) - e[2].elapsed_time(e[3]) for e in ev)
+    q = lambda v, f: v[min(len(v) - 1, int(f * (len(v) - 1) + 0.5))]
+    return q(ta, 0.5), q(tb, 0.5), q(d, 0.5), q(d, 0.75) - q(d, 0.25)
 
 
 def _ev_time(torch, fn, reps, before=None, stats=False):
@@ -130,7 +150,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gpt2_mlp")
-    ap.add_argument("--only", choices=["all", "fused", "streams", "producer", "copy"], default="all")
+    ap.add_argument("--only", choices=["all", "fused", "streams", "producer", "copy", "vendor"],
+                    default="all")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-autotune", action="store_true",
@@ -189,6 +210,17 @@ def main():
     def fused():
         mmar.fused(X, W, bias, res, P, p, seed, out=out)
 
+    if args.only == "vendor":
+        Cv = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        for _ in range(args.warmup):
+            torch.matmul(X, W, out=Cv)
+        torch.cuda.synchronize()
+        med, mean = _ev_time(torch, lambda: torch.matmul(X, W, out=Cv), args.steps)
+        print(json.dumps({"only": "vendor", "workload": w.name, "steps": args.steps,
+                          "median_us": round(med * 1e3, 2),
+                          "TFLOP/s": round(w.flops / (med * 1e-3) / 1e12, 2)}), flush=True)
+        return
+
     if args.only == "streams":
         def streams():
             mmar.fused_ex(X, W, bias, res, P, p, seed, "streams", out=out)
@@ -240,7 +272,8 @@ def main():
                    "plan": {"schedule": {1: "sequential", 2: "streams", 3: "persistent",
                                          4: "balanced"}[plan["schedule"]],
                             "chunk": list(plan["chunk"]), "ring": plan["ring"],
-                            "w_mode": {0: "direct", 1: "pretranspose"}[plan["w_mode"]]}},
+                            "w_mode": {0: "direct", 1: "pretranspose"}[plan["w_mode"]],
+                            "tile": {0: "256x128", 1: "256x192"}[plan["tile"]]}},
     }
     ksha = tile_kernel_sha()
     achieved = flops / (kernel_ms * 1e-3) / 1e12
@@ -266,6 +299,13 @@ def main():
         del flush
         T = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
         t_gemm = _ev_time(torch, lambda: mmar.gemm_only(X, W, P, out=T), reps)[0]
+        # the epilogue's exposed cost: fused and GEMM-only (the same persistent kernel on the
+        # plan's tile, storing T instead of applying the epilogue) alternated launch by launch
+        pers = lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "persistent", chunk=plan["chunk"]
+                                     if plan["schedule"] == 3 else (0, 0), w_mode="direct",
+                                     tile=plan["tile"], out=out)
+        pr_f, pr_g, pr_d, pr_iqr = _paired(torch, pers, lambda: mmar.gemm_only(X, W, P, out=T),
+                                           max(100, args.steps))
         parts = torch.empty((P, w.M, w.N), dtype=torch.float32, device="cuda")
         t_parts = _ev_time(torch, lambda: mmar.gemm_partials(X, W, P, out=parts), reps)[0]
         t_re = _ev_time(torch, lambda: mmar.reduce_epilogue_only(parts, bias, res, p, seed, out=out),
@@ -294,6 +334,12 @@ def main():
         t_bf16 = _ev_time(torch, lambda: mmar.fused_bf16(X, W, bias, res, P, p, seed, out=outb),
                           reps)[0]
         del outb
+        # vendor yardstick: hipBLASLt's plain bf16 GEMM at the block's shape through
+        # torch.matmul (bf16 out, no slices, no reduction order, no epilogue: strictly less
+        # work than the block)
+        Cv = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        t_vendor = _ev_time(torch, lambda: torch.matmul(X, W, out=Cv), reps)[0]
+        del Cv
         del parts
         # one rank's share on its own, at its real shape: the GEMM of one K-slice (P = 1,
         # K / P deep) with its fp32 output, what each of P tensor-parallel GPUs would run
@@ -313,6 +359,14 @@ def main():
                           reps)[0]
         t_mlp = _ev_time(torch, lambda: mmar.mlp(pd["X0"], pd["W1"], pd["b1"], W, bias, res, P, p,
                                                  seed, out=out, hidden=Hbuf), reps)[0]
+        # the same MLP in one call, H handed to the block in row chunks (producer of chunk
+        # c + 1 on this stream beside the block of chunk c on the library's second stream)
+        t_mlp_ch = {}
+        for cm in (w.M // 8, w.M // 4, w.M // 2):
+            if cm % 32 == 0 and cm > 0:
+                t_mlp_ch[cm] = _ev_time(torch, lambda: mmar.mlp_chunked(
+                    pd["X0"], pd["W1"], pd["b1"], W, bias, res, P, p, seed, chunk_m=cm, out=out,
+                    hidden=Hbuf), reps)[0]
         del pd, Hbuf
         torch.cuda.empty_cache()
         # the QKV projection in front of the GPT-2 attention block (bias, no activation):
@@ -369,11 +423,28 @@ def main():
         result["fused_us_stats"] = {"median": round(t_fused * 1e3, 2), "min": round(t_fused_min * 1e3, 2),
                                     "p90": round(t_fused_p90 * 1e3, 2),
                                     "median_cold_caches": round(t_cold * 1e3, 2)}
-        # hidden fractions on the persistent schedule, whose GEMM gemm_alone times (the
-        # balanced schedule moves part of the reduction out of the persistent kernel)
-        t_pers = t_fused if plan["schedule"] == 3 else t_dir
-        result["hidden_fraction"] = round(1.0 - (t_pers - t_gemm) / t_re, 4)
-        result["hidden_fraction_epilogue"] = round(1.0 - (t_pers - t_gemm) / t_epi, 4)
+        # Hidden fractions, from the paired protocol: d = median over pairs of
+        # (T_fused - T_gemm_alone) on the persistent kernel with the plan's tile (IQR beside
+        # it).  T_re_alone reduces P materialized partials, which the persistent schedule
+        # never writes: it removes the partial traffic rather than hiding it, so
+        # `hidden_fraction` is near 1 by construction; `hidden_fraction_epilogue` (against
+        # the epilogue alone over a materialized T) is the meaningful one.  Values are
+        # clamped to [0, 1] and `*_raw` keeps the unclamped figure.
+        def _frac(x):
+            return round(min(1.0, max(0.0, x)), 4)
+        result["paired_fused_minus_gemm"] = {"median_us": round(pr_d * 1e3, 2),
+                                             "iqr_us": round(pr_iqr * 1e3, 2),
+                                             "fused_us": round(pr_f * 1e3, 2),
+                                             "gemm_alone_us": round(pr_g * 1e3, 2),
+                                             "pairs": max(100, args.steps)}
+        result["hidden_fraction"] = _frac(1.0 - pr_d / t_re)
+        result["hidden_fraction_epilogue"] = _frac(1.0 - pr_d / t_epi)
+        result["hidden_fraction_epilogue_raw"] = round(1.0 - pr_d / t_epi, 4)
+        result["vendor_gemm_bf16"] = {"us": round(t_vendor * 1e3, 2),
+                                      "TFLOP/s": round(flops / (t_vendor * 1e-3) / 1e12, 2),
+                                      "what": f"torch.matmul [{w.M},{w.K}] x [{w.K},{w.N}] bf16 -> bf16 "
+                                              "(hipBLASLt), no epilogue",
+                                      "fused_over_vendor_time": round(t_fused / t_vendor, 3)}
         result["speedup_vs_sequential"] = round(t_seq / t_fused, 3)
         result["speedup_streams_vs_sequential"] = round(t_seq / t_str, 3)
         result["speedup_vs_unfused"] = round(t_unf / t_fused, 3)
@@ -386,7 +457,13 @@ def main():
                                    "TFLOP/s": round(flops / (t_prod * 1e-3) / 1e12, 2),
                                    "shape": f"[{w.M},{w.N}] x [{w.N},{w.K}] -> bf16 [{w.M},{w.K}]"}
         result["mlp"] = {"us": round(t_mlp * 1e3, 2),
-                         "TFLOP/s": round(2 * flops / (t_mlp * 1e-3) / 1e12, 2)}
+                         "TFLOP/s": round(2 * flops / (t_mlp * 1e-3) / 1e12, 2),
+                         "what": "producer (GeLU layer) then the block, two calls in sequence"}
+        result["mlp_chunked"] = {str(cm): {"us": round(t * 1e3, 2),
+                                           "TFLOP/s": round(2 * flops / (t * 1e-3) / 1e12, 2)}
+                                 for cm, t in t_mlp_ch.items()}
+        result["mlp_chunked"]["what"] = ("mmar_mlp with row chunks of chunk_m rows: the producer of "
+                                         "chunk c+1 beside the block of chunk c on a second stream")
         result["producer_qkv"] = {"us": round(t_qkv * 1e3, 2),
                                   "TFLOP/s": round(qkv_flops / (t_qkv * 1e-3) / 1e12, 2),
                                   "shape": f"[{qw.M},{qw.N}] x [{qw.N},{3 * qw.K}] -> bf16 "

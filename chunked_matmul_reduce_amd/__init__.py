@@ -64,6 +64,8 @@ _SIGNATURES = {
     "mmar_fused_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32,
                                           _I32, _I32, _I32, _I32, _I32, _P]),
     "mmar_noalloc_workspace_capacity": (_SZ, []),
+    "mmar_mlp": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _U64,
+                                _I32, _P]),
     "mmar_last_error": (ctypes.c_char_p, []),
     "mmar_version": (ctypes.c_char_p, []),
     "mmar_release": (ctypes.c_int, []),
@@ -373,6 +375,30 @@ def mlp(X, W1, b1, W2, b2, residual, P, p_drop, seed, out=None, hidden=None, str
     (out, H)."""
     H = gelu_linear(X, W1, b1, out=hidden, stream=stream)
     return fused(H, W2, b2, residual, P, p_drop, seed, out=out, stream=stream), H
+
+
+def mlp_chunked(X, W1, b1, W2, b2, residual, P, p_drop, seed, chunk_m=0, out=None, hidden=None,
+                stream=None):
+    """mmar_mlp: the same MLP in one call; chunk_m > 0 hands H to the block row chunk by row
+    chunk (producer of chunk c+1 beside the block of chunk c, two streams).  Returns
+    (out, H)."""
+    torch = _torch()
+    if X.dim() != 2 or W1.dim() != 2 or W2.dim() != 2:
+        raise ValueError("X must be [M, D], W1 [D, K], W2 [K, N]")
+    M, D = (int(v) for v in X.shape)
+    K = int(W1.shape[1])
+    N = int(W2.shape[1])
+    if hidden is None:
+        hidden = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    out = _out(out, (M, N), X)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_mlp(_bits(X, "X", (M, D)), _bits(W1, "W1", (D, K)), _bits(b1, "b1", (K,)),
+                          _bits(W2, "W2", (K, N)), _bits(b2, "b2", (N,)),
+                          _bits(residual, "residual", (M, N)), _bits(hidden, "hidden", (M, K)),
+                          out.data_ptr(), M, D, K, N, int(P), float(p_drop),
+                          int(seed) & (2 ** 64 - 1), int(chunk_m), _stream(X.device, stream))
+    _check(rc)
+    return out, hidden
 
 
 def adam_step(grads, param, m, v, step, lr, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0,

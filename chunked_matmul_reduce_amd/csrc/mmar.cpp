@@ -1081,15 +1081,30 @@ static int64_t linear_wide_columns(const DevState* st, int64_t M, int64_t N) {
     return best_nw;
 }
 
-// The producer MatMul over output columns [n0, n0 + cols) with one tile width.
-static int run_linear_columns(const DevState* st, const Call& c, int mode, int n0, int cols,
-                              hipStream_t s) {
+// The producer MatMul over output rows [m0, m0 + rows) and columns [n0, n0 + cols) with
+// one tile width.
+static int run_linear_columns(const DevState* st, const Call& c, int mode, int m0, int rows,
+                              int n0, int cols, hipStream_t s) {
     const int bk = bk_for(c.s);
-    const int M = static_cast<int>(c.s.M);
-    TileArgs a = tile_args(c, 0, n0, M, cols, M, cols);
-    a.total_items = static_cast<int32_t>(tiles_in(M, cols, mmar::tile_bn(mode)));
+    TileArgs a = tile_args(c, m0, n0, rows, cols, rows, cols);
+    a.total_items = static_cast<int32_t>(tiles_in(rows, cols, mmar::tile_bn(mode)));
     MMAR_HIP(mmar::launch_tile(mode, bk, c.w_t, mmar::kTile128, a,
                                grid_for(st, mode, bk, a.total_items), s));
+    return MMAR_OK;
+}
+
+// The producer MatMul over output rows [m0, m0 + rows), every column: the leading columns
+// on 256 x 256 tiles and the rest on 256 x 128 (linear_wide_columns for that row count).
+static int run_linear_rows(const DevState* st, const Call& c, int m0, int rows, hipStream_t s) {
+    const int N = static_cast<int>(c.s.N);
+    const int64_t nw = linear_wide_columns(st, rows, N);
+    int rc;
+    if (nw > 0 &&
+        (rc = run_linear_columns(st, c, mmar::kModeLinearWide, m0, rows, 0, static_cast<int>(nw), s)))
+        return rc;
+    if (nw < N)
+        return run_linear_columns(st, c, mmar::kModeLinear, m0, rows, static_cast<int>(nw),
+                                  static_cast<int>(N - nw), s);
     return MMAR_OK;
 }
 
@@ -1119,19 +1134,89 @@ int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint
     c.act = activation == MMAR_ACT_GELU_TANH ? mmar::kActGeluTanh : mmar::kActNone;
     c.s = s;
     c.w_t = false;
-    const hipStream_t hs = static_cast<hipStream_t>(stream);
-    const int64_t nw = linear_wide_columns(st, M, N);
-    if (nw > 0 && (rc = run_linear_columns(st, c, mmar::kModeLinearWide, 0, static_cast<int>(nw), hs)))
-        return rc;
-    if (nw < N)
-        return run_linear_columns(st, c, mmar::kModeLinear, static_cast<int>(nw),
-                                  static_cast<int>(N - nw), hs);
-    return MMAR_OK;
+    return run_linear_rows(st, c, 0, static_cast<int>(M), static_cast<hipStream_t>(stream));
 }
 
 int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
                      int64_t M, int64_t N, int64_t K, void* stream) {
     return mmar_linear(X, W, bias, H, M, N, K, MMAR_ACT_GELU_TANH, stream);
+}
+
+int mmar_mlp(const uint16_t* X0, const uint16_t* W1, const uint16_t* b1, const uint16_t* W2,
+             const uint16_t* b2, const uint16_t* residual, uint16_t* H, float* out, int64_t M,
+             int64_t D, int64_t K, int64_t N, int32_t P, float p_drop, uint64_t seed,
+             int32_t chunk_m, void* stream) {
+    g_err.clear();
+    const Shape sp{M, K, D, 1};   // producer: [M, D] x [D, K]
+    const Shape sb{M, N, K, P};   // block: [M, K] x [K, N], P slices
+    int rc;
+    if ((rc = check_shape(sp)) || (rc = check_shape(sb))) return rc;
+    if (chunk_m < 0 || (chunk_m != 0 && (chunk_m % 32 != 0 || M % chunk_m != 0)))
+        return fail(MMAR_EINVAL, "chunk_m must be 0 or a multiple of 32 dividing M");
+    if ((rc = check_ptr(X0, "X0")) || (rc = check_ptr(W1, "W1")) || (rc = check_ptr(b1, "b1")) ||
+        (rc = check_ptr(H, "H")))
+        return rc;
+    const size_t hb = static_cast<size_t>(M * K) * 2;
+    if (overlaps(H, hb, X0, static_cast<size_t>(M * D) * 2) ||
+        overlaps(H, hb, W1, static_cast<size_t>(D * K) * 2) ||
+        overlaps(H, hb, b1, static_cast<size_t>(K) * 2) ||
+        overlaps(H, hb, W2, static_cast<size_t>(K * N) * 2) ||
+        overlaps(H, hb, b2, static_cast<size_t>(N) * 2) ||
+        overlaps(H, hb, residual, static_cast<size_t>(M * N) * 2) ||
+        overlaps(H, hb, out, static_cast<size_t>(M * N) * 4))
+        return fail(MMAR_EINVAL, "H overlaps another argument");
+    Call cb;
+    if ((rc = check_call(H, W2, b2, residual, out, sb, p_drop, seed, 0, 0, &cb))) return rc;
+    const size_t ob = static_cast<size_t>(M * N) * 4;
+    if (overlaps(out, ob, X0, static_cast<size_t>(M * D) * 2) ||
+        overlaps(out, ob, W1, static_cast<size_t>(D * K) * 2) ||
+        overlaps(out, ob, b1, static_cast<size_t>(K) * 2))
+        return fail(MMAR_EINVAL, "out overlaps an input");
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    Call cp;
+    cp.X = X0;
+    cp.W = W1;
+    cp.bias = b1;
+    cp.hout = H;
+    cp.act = mmar::kActGeluTanh;
+    cp.s = sp;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int bk = bk_for(sb);
+    // the block over rows [m0, m0 + rows): the persistent kernel on that region (the
+    // Philox counters use global indices, so the bits are those of the whole block)
+    auto block_rows = [&](int m0, int rows, hipStream_t on) -> int {
+        TileArgs a = tile_args(cb, m0, 0, rows, static_cast<int>(N), rows, static_cast<int>(N));
+        a.total_items = static_cast<int32_t>(tiles_in(rows, static_cast<int>(N)));
+        MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, false, mmar::kTile128, a,
+                                   grid_for(st, mmar::kModeFused, bk, a.total_items), on));
+        return MMAR_OK;
+    };
+    if (chunk_m == 0 || chunk_m == M) {   // the producer, then the block
+        if ((rc = run_linear_rows(st, cp, 0, static_cast<int>(M), s))) return rc;
+        return block_rows(0, static_cast<int>(M), s);
+    }
+    // Row chunks: the producer of chunk c on the caller's stream, the block of chunk c on
+    // the side stream once that chunk of H is written, so the producer of chunk c + 1 runs
+    // beside the block of chunk c (H arriving chunk by chunk).  The side stream and events
+    // are shared per device: the enqueue sequence runs under the lock.
+    std::lock_guard<std::mutex> lk(st->side_mu);
+    if ((rc = ensure_streams(st))) return rc;
+    MMAR_HIP(hipStreamWaitEvent(s, st->ev_side_done, 0));   // earlier side work first
+    const int chunks = static_cast<int>(M / chunk_m);
+    int last_slot = 0;
+    for (int ch = 0; ch < chunks; ++ch) {
+        const int slot = ch % kMaxRing;
+        if ((rc = run_linear_rows(st, cp, ch * chunk_m, chunk_m, s))) return rc;
+        MMAR_HIP(hipEventRecord(st->ev_gemm[slot], s));
+        MMAR_HIP(hipStreamWaitEvent(st->side, st->ev_gemm[slot], 0));
+        if ((rc = block_rows(ch * chunk_m, chunk_m, st->side))) return rc;
+        MMAR_HIP(hipEventRecord(st->ev_red[slot], st->side));
+        last_slot = slot;
+    }
+    MMAR_HIP(hipEventRecord(st->ev_side_done, st->side));
+    MMAR_HIP(hipStreamWaitEvent(s, st->ev_red[last_slot], 0));
+    return MMAR_OK;
 }
 
 int mmar_unfused(const uint16_t* X, const uint16_t* W, const uint16_t* bias,

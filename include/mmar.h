@@ -240,6 +240,26 @@ int mmar_gelu_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
 int mmar_linear(const uint16_t* X, const uint16_t* W, const uint16_t* bias, uint16_t* H,
                 int64_t M, int64_t N, int64_t K, int32_t activation, void* stream);
 
+/* The MLP around the block, producer and block in one call (the block sits between two
+ * MatMuls: practices record SOTA-059, "Where it stops being free"; CoCoNet overlaps a
+ * producer with the collective that consumes it: LIT-735, "Key takeaways", first bullet):
+ *   H   = GeLU(X0 . W1 + b1)          X0 [M, D], W1 [D, K], b1 [K], H [M, K] bf16 (written)
+ *   out = residual + dropout_p(b2 + sum_p H[:, K_p] . W2[K_p, :])
+ *                                     W2 [K, N], b2 [N], residual [M, N] bf16, out [M, N] fp32
+ * with the arithmetic of mmar_gelu_linear and mmar_fused (same bits as calling the two in
+ * turn).  chunk_m = 0: the producer over all rows, then the block, on `stream`.  chunk_m a
+ * multiple of 32 dividing M: row chunks, the producer of chunk c on `stream` and the block
+ * of chunk c on the library's side stream once that chunk of H is written, so the producer
+ * of the next chunk runs beside it (H handed over chunk by chunk, the way an all-gathered
+ * input arrives); `stream` waits for the side stream before the call returns.
+ * Preconditions as mmar_gelu_linear (M, K, D) and mmar_fused (M, N, K, P); H must not
+ * overlap any other argument, out no input.  Uses no workspace; the chunked form uses the
+ * side stream (serialized per device). */
+int mmar_mlp(const uint16_t* X0, const uint16_t* W1, const uint16_t* b1, const uint16_t* W2,
+             const uint16_t* b2, const uint16_t* residual, uint16_t* H, float* out, int64_t M,
+             int64_t D, int64_t K, int64_t N, int32_t P, float p_drop, uint64_t seed,
+             int32_t chunk_m, void* stream);
+
 /* The data-parallel side of the CoCoNet record ("Key takeaways", fifth bullet: the
  * gradient ReduceScatter, the optimizer and the parameter AllGather fused) folded onto
  * one GPU, one HBM pass:

@@ -75,14 +75,13 @@ def test_bf16_output_edge_probabilities():
 
 
 @pytest.mark.parametrize("name", ["gpt2_mlp"])
-def test_bf16_output_full_size_sampled_rows(name):
+def test_bf16_output_full_size_all_rows(name):
     w = WORKLOADS[name]
     inp = make_inputs(name)
     bits, rounded = _run_both(inp, w.P, inp["p_drop"], w.seed)
     assert np.array_equal(bits, rounded)
-    rng = np.random.default_rng(w.seed + 1)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, w.M - 1], rng.choice(w.M, 40, replace=False)]))
-    frac = _check(inp, w.P, inp["p_drop"], w.seed, bits, rows=rows)
+    print(name, "bf16 output: oracle over all rows", flush=True)
+    frac = _check(inp, w.P, inp["p_drop"], w.seed, bits)
     print(name, "near-tie fraction", frac, flush=True)
     torch.cuda.empty_cache()
 

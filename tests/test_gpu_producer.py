@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from oracle import producer
-from workload import WORKLOADS, make_producer_inputs, make_qkv_inputs, make_random_inputs
+from workload import WORKLOADS, make_inputs, make_producer_inputs, make_qkv_inputs, make_random_inputs
 from helpers import assert_within_tol, dev, host
 
 torch = pytest.importorskip("torch")
@@ -44,17 +44,26 @@ def test_producer_against_oracle(M, K, N):
     assert ties < 0.7 * M * N
 
 
-def test_producer_full_size_sampled_rows():
-    """The GPT-2 MLP block's first layer: [8192, 3072] x [3072, 12288]."""
+def _check_producer_all_rows(hb, X, W, b, activation="gelu_tanh", block=2048):
+    """Every row of a bf16 producer output against the oracle, a block of rows at a time
+    (bounded host memory)."""
+    ties = 0
+    for r0 in range(0, hb.shape[0], block):
+        rows = np.arange(r0, min(hb.shape[0], r0 + block))
+        h, _, bound = producer.producer(X, W, b, rows=rows, activation=activation)
+        ties += producer.check_bf16_output(hb[rows], h, bound)
+    return ties
+
+
+def test_producer_full_size_all_rows():
+    """The GPT-2 MLP block's first layer: [8192, 3072] x [3072, 12288], every element."""
     w = WORKLOADS["gpt2_mlp"]
     pin = make_producer_inputs(w)
     X0, W1, b1 = (dev(pin[k], torch) for k in ("X0", "W1", "b1"))
     H = mmar.gelu_linear(X0, W1, b1)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(7)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 8191], rng.choice(w.M, 90, replace=False)]))
-    h, _, bound = producer.producer(pin["X0"], pin["W1"], pin["b1"], rows=rows)
-    producer.check_bf16_output(_h_bits(H)[rows], h, bound)
+    print("producer full size: oracle over all rows", flush=True)
+    _check_producer_all_rows(_h_bits(H), pin["X0"], pin["W1"], pin["b1"])
 
 
 def test_mlp_tiny_against_oracle_and_bits_of_parts():
@@ -77,6 +86,77 @@ def test_mlp_tiny_against_oracle_and_bits_of_parts():
     out2 = mmar.fused(H, W2, b2, R, P, p, seed)
     torch.cuda.synchronize()
     assert np.array_equal(host(out).view(np.uint32), host(out2).view(np.uint32))
+
+
+@pytest.mark.parametrize("chunk", [0, 32, 64, 128])
+def test_mlp_chunked_tiny_bits_and_oracle(chunk):
+    """mmar_mlp (producer and block in one call; with row chunks, the block of chunk c on a
+    second stream beside the producer of chunk c + 1) gives mlp()'s bits for H and out,
+    and both match the oracles."""
+    M, D, F, P = 256, 256, 512, 4
+    a = make_random_inputs(M, D, F, seed=31)
+    c = make_random_inputs(M, F, D, seed=32)
+    X0, W1, b1 = (dev(a[k], torch) for k in ("X", "W", "bias"))
+    W2, b2, R = (dev(c[k], torch) for k in ("W", "bias", "residual"))
+    p, seed = np.float32(0.1), 12345
+    out_ref, H_ref = mmar.mlp(X0, W1, b1, W2, b2, R, P, p, seed)
+    out, H = mmar.mlp_chunked(X0, W1, b1, W2, b2, R, P, p, seed, chunk_m=chunk)
+    torch.cuda.synchronize()
+    assert np.array_equal(_h_bits(H), _h_bits(H_ref))
+    assert np.array_equal(host(out).view(np.uint32), host(out_ref).view(np.uint32))
+    hb = _h_bits(H)
+    h, _, bound = producer.producer(a["X"], a["W"], a["bias"])
+    producer.check_bf16_output(hb, h, bound)
+    ora, _ = oracle.run(hb, c["W"], c["bias"], c["residual"], P, p, seed)
+    assert_within_tol(host(out), ora)
+
+
+def test_mlp_chunked_full_size_gpt2():
+    """The GPT-2 8.3B MLP (first layer [8192, 3072] x [3072, 12288] + GeLU, then the block,
+    P = 16): the chunked pipeline at several row chunks gives the bits of the two calls in
+    turn; H against the producer oracle and out against the block oracle on every element."""
+    w = WORKLOADS["gpt2_mlp"]
+    pin = make_producer_inputs(w)
+    inp = make_inputs(w)
+    X0, W1, b1 = (dev(pin[k], torch) for k in ("X0", "W1", "b1"))
+    W2, b2, R = (dev(inp[k], torch) for k in ("W", "bias", "residual"))
+    p, seed = inp["p_drop"], w.seed
+    out_ref, H_ref = mmar.mlp(X0, W1, b1, W2, b2, R, w.P, p, seed)
+    torch.cuda.synchronize()
+    ref_out, ref_h = host(out_ref).view(np.uint32).copy(), _h_bits(H_ref).copy()
+    for chunk in (0, 1024, 2048):
+        print("mlp chunked", chunk, flush=True)
+        out, H = mmar.mlp_chunked(X0, W1, b1, W2, b2, R, w.P, p, seed, chunk_m=chunk,
+                                  out=out_ref, hidden=H_ref)
+        torch.cuda.synchronize()
+        assert np.array_equal(_h_bits(H), ref_h), chunk
+        assert np.array_equal(host(out).view(np.uint32), ref_out), chunk
+    del X0, W1, b1, W2, b2, R
+    torch.cuda.empty_cache()
+    print("mlp full size: producer oracle over all rows", flush=True)
+    _check_producer_all_rows(ref_h, pin["X0"], pin["W1"], pin["b1"])
+    print("mlp full size: block oracle over all rows", flush=True)
+    ora, _ = oracle.run(ref_h, inp["W"], inp["bias"], inp["residual"], w.P, p, seed)
+    assert_within_tol(ref_out.view(np.float32), ora)
+
+
+def test_mlp_chunked_rejects_bad_arguments():
+    X = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    W1 = torch.zeros((256, 512), dtype=torch.bfloat16, device="cuda")
+    b1 = torch.zeros((512,), dtype=torch.bfloat16, device="cuda")
+    W2 = torch.zeros((512, 256), dtype=torch.bfloat16, device="cuda")
+    b2 = torch.zeros((256,), dtype=torch.bfloat16, device="cuda")
+    R = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(mmar.MmarError):
+        mmar.mlp_chunked(X, W1, b1, W2, b2, R, 4, 0.1, 1, chunk_m=48)   # not a multiple of 32
+    with pytest.raises(mmar.MmarError):
+        mmar.mlp_chunked(X, W1, b1, W2, b2, R, 3, 0.1, 1)                # P does not divide K
+    H = torch.empty((64, 512), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((64, 256), dtype=torch.float32, device="cuda")
+    rc = mmar.lib.mmar_mlp(X.data_ptr(), W1.data_ptr(), b1.data_ptr(), W2.data_ptr(), b2.data_ptr(),
+                           R.data_ptr(), X.data_ptr(), out.data_ptr(), 64, 256, 512, 256, 4, 0.1, 1,
+                           0, None)
+    assert rc == mmar.EINVAL                                           # H overlaps X0
 
 
 def test_producer_rejects_bad_arguments():
@@ -113,18 +193,16 @@ def test_linear_without_activation_against_oracle(M, K, N):
     assert np.array_equal(_h_bits(Hg), _h_bits(Hg2))
 
 
-def test_linear_qkv_full_size_sampled_rows():
+def test_linear_qkv_full_size_all_rows():
     """The GPT-2 attention block's QKV projection: [8192, 3072] x [3072, 9216], bias, no
-    activation."""
+    activation; every element."""
     w = WORKLOADS["gpt2_attn"]
     pin = make_qkv_inputs(w)
     X0, Wq, bq = (dev(pin[k], torch) for k in ("X0", "Wqkv", "bqkv"))
     H = mmar.linear(X0, Wq, bq, "none")
     torch.cuda.synchronize()
-    rng = np.random.default_rng(8)
-    rows = np.unique(np.concatenate([[0, 1, 255, 256, 4095, 8191], rng.choice(w.M, 60, replace=False)]))
-    h, _, bound = producer.producer(pin["X0"], pin["Wqkv"], pin["bqkv"], rows=rows, activation="none")
-    producer.check_bf16_output(_h_bits(H)[rows], h, bound)
+    print("qkv full size: oracle over all rows", flush=True)
+    _check_producer_all_rows(_h_bits(H), pin["X0"], pin["Wqkv"], pin["bqkv"], activation="none")
 
 
 def test_linear_rejects_an_unknown_activation():
