@@ -342,12 +342,14 @@ def main():
         del Cv
         del parts
         # one rank's share on its own, at its real shape: the GEMM of one K-slice (P = 1,
-        # K / P deep) with its fp32 output, what each of P tensor-parallel GPUs would run
-        # before the exchange
+        # K / P deep) with its fp32 output (the partials kernel), what each of P
+        # tensor-parallel GPUs would run before the exchange
         ks = w.K // P
         Xr, Wr = X[:, :ks].contiguous(), W[:ks].contiguous()
-        t_rank = _ev_time(torch, lambda: mmar.gemm_only(Xr, Wr, 1, out=T), reps)[0]
-        del Xr, Wr, T
+        # the per-rank kernel is the partials mode with one slice: S_p = X_p W_p, fp32
+        T1 = T.view(1, w.M, w.N)
+        t_rank = _ev_time(torch, lambda: mmar.gemm_partials(Xr, Wr, 1, out=T1), reps)[0]
+        del Xr, Wr, T, T1
         torch.cuda.empty_cache()
         # the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16) and the
         # whole MLP (producer then block), on the producer's seeded inputs

@@ -753,6 +753,39 @@ void tile_kernel(TileArgs a) {
                 });
             else
                 store_all([&](int64_t e, float4 o) { *reinterpret_cast<float4*>(a.out + e) = o; });
+        } else if constexpr (MODE == kModePartials) {
+            // The slice partial S_p through the idle copy ring to whole-row stores: each
+            // wave writes its 64 x 128 block into its own 32 KB (16-byte chunk c of row r at
+            // chunk c ^ (r % 32) of that row, so the 32 rows a store instruction of the MFMA
+            // layout touches hit different banks), reads it back two rows (2 x 512 bytes)
+            // per instruction and stores them contiguously into the partials [P][RM][RN];
+            // then a barrier, so no wave's next copies overwrite a block still being read.
+            static_assert(C::RW == 64 && C::BN == 128 && C::NW * 32768 <= C::RING_BYTES,
+                          "staging layout of the partials tile");
+            float* const stg = reinterpret_cast<float*>(smem) + uwave * (64 * 128);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int r = 32 * mb + l32, c = 8 * nb + 2 * g + h;   // 16-byte chunk
+                        const f32x16& acc = S[nb][mb];
+                        reinterpret_cast<float4*>(stg + r * 128)[c ^ (r & 31)] =
+                            make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+                    }
+            float* const dst0 = a.ws + static_cast<int64_t>(p_lo) * a.RM * a.RN +
+                                static_cast<int64_t>(m0 + C::RW * wm - a.rm0) * a.RN + (n0 - a.rn0);
+            const int c = lane & 31;
+#pragma unroll 8
+            for (int i = 0; i < 32; ++i) {
+                const int r = 2 * i + h;   // row of this lane within the wave's 64
+                const float4 v = reinterpret_cast<const float4*>(stg + r * 128)[c ^ (r & 31)];
+                if (C::RW * wm + r < rows && 4 * c < cols)
+                    *reinterpret_cast<float4*>(dst0 + static_cast<int64_t>(r) * a.RN + 4 * c) = v;
+            }
+            MMAR_WAIT_VM_LDS(63);   // lgkmcnt(0): this wave's ring reads have returned
+            wg_barrier();
         } else {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
@@ -763,16 +796,9 @@ void tile_kernel(TileArgs a) {
                         if (!col_ok(nb) || !row_ok(mb)) continue;
                         const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
                         const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
-                        const f32x16& acc = (MODE == kModePartials) ? S[nb][mb] : T[nb][mb];
-                        const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2],
-                                                     acc[4 * g + 3]);
-                        if (MODE == kModeReduced) {
-                            *reinterpret_cast<float4*>(a.out + m * a.N + n) = v;
-                        } else {
-                            float* dst = a.ws + static_cast<int64_t>(p_lo) * a.RM * a.RN +
-                                         (m - a.rm0) * a.RN + (n - a.rn0);
-                            *reinterpret_cast<float4*>(dst) = v;
-                        }
+                        const f32x16& acc = T[nb][mb];
+                        *reinterpret_cast<float4*>(a.out + m * a.N + n) = make_float4(
+                            acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
                     }
         }
     }
