@@ -375,11 +375,14 @@ void load_plan_cache_locked() {
         char arch[64] = {0};
         long long M, N, K;
         int P, sched, cm, cn, ring, wmode, tile;
-        if (std::sscanf(line,
-                        " {\"arch\": \"%63[^\"]\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
-                        "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d, "
-                        "\"w_mode\": %d, \"tile\": %d",
-                        arch, &M, &N, &K, &P, &sched, &cm, &cn, &ring, &wmode, &tile) == 11) {
+        float margin = 0.0f;
+        const int got = std::sscanf(
+            line,
+            " {\"arch\": \"%63[^\"]\", \"M\": %lld, \"N\": %lld, \"K\": %lld, \"P\": %d, "
+            "\"schedule\": %d, \"chunk_m\": %d, \"chunk_n\": %d, \"ring\": %d, "
+            "\"w_mode\": %d, \"tile\": %d, \"margin_ms\": %f",
+            arch, &M, &N, &K, &P, &sched, &cm, &cn, &ring, &wmode, &tile, &margin);
+        if (got >= 11) {   // entries written without a margin keep 0
             Plan p;
             p.sched = sched;
             p.cm = cm;
@@ -387,6 +390,7 @@ void load_plan_cache_locked() {
             p.ring = ring;
             p.wmode = wmode;
             p.tile = tile;
+            p.margin_ms = got == 12 ? margin : 0.0f;
             if (plan_is_valid(Shape{M, N, K, P}, p)) g_plans[PlanKey(arch, M, N, K, P)] = p;
         }
     }
@@ -770,9 +774,12 @@ void med_iqr(std::vector<float> t, float* med, float* iqr) {
     *iqr = t[(3 * n) / 4] - t[n / 4];
 }
 
-// Times every candidate plan `rounds` times, interleaved (round r runs every candidate once,
-// in order), so clock drift and thermal state affect all candidates alike.  times[i] gets
-// candidate i's per-call durations in ms.
+// Times every candidate plan `rounds` times, interleaved (round r runs every candidate once)
+// so that clock drift and thermal state affect all candidates alike.  Each round starts
+// with one untimed call (the first launch after the round's synchronization meets an idle
+// GPU) and runs the candidates in an order rotated by one per round, so no candidate is
+// always first or always after the same one.  times[i] gets candidate i's per-call
+// durations in ms.
 int time_plans(DevState* st, const Call& c, const std::vector<Plan>& plans, int rounds,
                hipStream_t s, std::vector<std::vector<float>>* times) {
     const size_t n = plans.size();
@@ -784,7 +791,9 @@ int time_plans(DevState* st, const Call& c, const std::vector<Plan>& plans, int 
     for (size_t i = 0; i < n && !rc; ++i)   // warm-up: one call of each
         rc = run_plan(st, c, plans[i], kRunFused, nullptr, 0, s);
     for (int r = 0; r < rounds && !rc; ++r) {
-        for (size_t i = 0; i < n && !rc; ++i) {
+        rc = run_plan(st, c, plans[static_cast<size_t>(r) % n], kRunFused, nullptr, 0, s);
+        for (size_t j = 0; j < n && !rc; ++j) {
+            const size_t i = (j + static_cast<size_t>(r)) % n;
             if (hipEventRecord(ev[2 * i], s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
             if (!rc) rc = run_plan(st, c, plans[i], kRunFused, nullptr, 0, s);
             if (!rc && hipEventRecord(ev[2 * i + 1], s) != hipSuccess)
@@ -1330,9 +1339,14 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
 
-    // candidate plans; the first is the incumbent (the default plan)
+    // candidate plans; the first is the incumbent (the default plan), and no other
+    // candidate repeats it
     std::vector<Plan> cands;
     cands.push_back(resolve(s, default_plan(s, st->cus), st->cus));
+    auto same = [](const Plan& a, const Plan& b) {
+        return a.sched == b.sched && a.cm == b.cm && a.cn == b.cn && a.ring == b.ring &&
+               a.wmode == b.wmode && a.tile == b.tile && a.hm == b.hm && a.hn == b.hn;
+    };
     for (int tile : {MMAR_TILE_256x128, MMAR_TILE_256x192})
         for (int wm : {MMAR_W_DIRECT, MMAR_W_PRETRANSPOSE}) {
             for (int cm : divisors32(M, {1, 2, 4}))
@@ -1368,6 +1382,16 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
         p.sched = MMAR_SCHED_SEQUENTIAL;
         p.wmode = default_wmode(s);
         cands.push_back(resolve(s, p, st->cus));
+    }
+
+    {
+        std::vector<Plan> uniq;
+        for (const Plan& p : cands) {
+            bool dup = false;
+            for (const Plan& q : uniq) dup = dup || same(p, q);
+            if (!dup) uniq.push_back(p);
+        }
+        cands.swap(uniq);
     }
 
     // library-owned inputs with the value spread of the block's inputs

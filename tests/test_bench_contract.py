@@ -29,6 +29,20 @@ def test_traffic_summary_matches_its_workload():
     kib = cal["copy_bytes"] / 1024
     assert abs(cal["fetch_factor"] - kib / cal["fetch_size_kib"]) < 1e-3
     assert abs(cal["write_factor"] - kib / cal["write_size_kib"]) < 1e-3
+    # the request-counter derivation: bytes are requests times their sizes, the copy of
+    # 1 GiB reads and writes 1 GiB, and the fused kernel's figure agrees with the calibrated
+    # one within the box-to-box spread
+    rq = d["request_counters"]
+    f = rq["fused"]
+    assert f["read_bytes_per_launch"] == (128 * f["TCC_EA0_RDREQ_128B"] + 64 * f["TCC_EA0_RDREQ_64B"]
+                                          + 32 * f["TCC_EA0_RDREQ_32B"])
+    assert f["write_bytes_per_launch"] == (64 * f["TCC_EA0_WRREQ_64B"]
+                                           + 32 * (f["TCC_EA0_WRREQ"] - f["TCC_EA0_WRREQ_64B"]))
+    assert f["traffic_bytes_per_launch"] == f["read_bytes_per_launch"] + f["write_bytes_per_launch"]
+    cp = rq["copy_1GiB"]
+    assert abs(cp["read_bytes"] / cal["copy_bytes"] - 1) < 1e-3
+    assert abs(cp["write_bytes"] / cal["copy_bytes"] - 1) < 1e-3
+    assert abs(f["traffic_bytes_per_launch"] / d["traffic_bytes_per_launch"] - 1) < 0.03
     # the bench reports the counters only while they describe the current kernel sources
     t = bench._traffic(bench.tile_kernel_sha())
     assert t is None or t == d["traffic_bytes_per_launch"]
