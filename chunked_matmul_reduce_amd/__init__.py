@@ -61,6 +61,8 @@ _SIGNATURES = {
     "mmar_get_plan": (ctypes.c_int, [_I64, _I64, _I64, _I32, ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                      ctypes.POINTER(_I32), ctypes.POINTER(_I32), ctypes.POINTER(_I32),
                                      ctypes.POINTER(_I32)]),
+    "mmar_fused_strided": (ctypes.c_int, [_P, _I64, _P, _I64, _P, _P, _I64, _P, _I64, _I64, _I64, _I64,
+                                          _I32, _F, _U64, _U64, _P]),
     "mmar_fused_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I32, _F, _U64, _I32,
                                           _I32, _I32, _I32, _I32, _I32, _P]),
     "mmar_noalloc_workspace_capacity": (_SZ, []),
@@ -266,6 +268,46 @@ def fused_noalloc(X, W, bias, residual, P, p_drop, seed, schedule, chunk=(0, 0),
 
 def noalloc_workspace_capacity() -> int:
     return int(lib.mmar_noalloc_workspace_capacity())
+
+
+def _rows(t, name, shape, dtypes, align):
+    """Data pointer and leading dimension of a 2-D tensor whose rows are contiguous."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise TypeError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.stride(1) != 1:
+        raise ValueError(f"{name} must have contiguous rows (stride 1 along its last dimension)")
+    ld = int(t.stride(0)) if shape[0] > 1 else int(shape[1])
+    if ld % align:
+        raise ValueError(f"{name}'s leading dimension {ld} is not a multiple of {align}")
+    return t.data_ptr(), ld
+
+
+def fused_strided(X, W, bias, residual, P, p_drop, seed, philox_offset=0, out=None,
+                  stream=None):
+    """mmar_fused_strided: the block over row-strided views (each 2-D tensor with
+    contiguous rows and any row stride: a column block of a wider buffer, say) and with
+    the dropout mask's Philox counter words 2-3 set to ``philox_offset``.  ``out`` may be a
+    row-strided float32 view; a new dense one is allocated when it is None."""
+    torch = _torch()
+    M, N, K = _shapes(X, W, P)
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    xp, ldx = _rows(X, "X", (M, K), b16, 8)
+    wp, ldw = _rows(W, "W", (K, N), b16, 8)
+    rp, ldr = _rows(residual, "residual", (M, N), b16, 4)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    op, ldo = _rows(out, "out", (M, N), (torch.float32,), 4)
+    with torch.cuda.device(X.device):
+        rc = lib.mmar_fused_strided(xp, ldx, wp, ldw, _bits(bias, "bias", (N,)), rp, ldr, op, ldo,
+                                    M, N, K, int(P), float(p_drop), int(seed) & (2 ** 64 - 1),
+                                    int(philox_offset) & (2 ** 64 - 1), _stream(X.device, stream))
+    _check(rc)
+    return out
 
 
 def fused_nt(X, Wt, bias, residual, P, p_drop, seed, chunk=(0, 0), out=None, stream=None):

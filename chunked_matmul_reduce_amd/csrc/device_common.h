@@ -52,12 +52,14 @@ __device__ __forceinline__ float epi1(float t, float b, float r, uint32_t word,
     return keep ? __fadd_rn(r, y) : r;
 }
 
-// Epilogue of four consecutive outputs starting at linear index e (e % 4 == 0).
+// Epilogue of four consecutive outputs starting at linear index e (e % 4 == 0; e = m N + n
+// for output (m, n) whatever the buffers' leading dimensions): the Philox block at counter
+// (lo32(e / 4), hi32(e / 4), offset words) gives the four elements' words.
 __device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int64_t e,
                                             const DropParams& d) {
     const uint64_t g = static_cast<uint64_t>(e) >> 2;
     const uint4 w = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32),
-                                  0u, 0u, d.key0, d.key1);
+                                  d.ctr2, d.ctr3, d.key0, d.key1);
     float4 o;
     o.x = epi1(t.x, bf16_lo(bias.x), bf16_lo(res.x), w.x, d);
     o.y = epi1(t.y, bf16_hi(bias.x), bf16_hi(res.x), w.y, d);

@@ -123,10 +123,11 @@ int check_sched(int32_t sched, int32_t ring, int32_t wmode, int32_t tile) {
     return MMAR_OK;
 }
 
-int check_ptr(const void* p, const char* name) {
+int check_ptr(const void* p, const char* name, unsigned align = 16) {
     if (p == nullptr) return fail(MMAR_EINVAL, std::string(name) + " is NULL");
-    if (reinterpret_cast<uintptr_t>(p) % 16 != 0)
-        return fail(MMAR_EALIGN, std::string(name) + " is not 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(p) % align != 0)
+        return fail(MMAR_EALIGN, std::string(name) + " is not " + std::to_string(align) +
+                                     "-byte aligned");
     return MMAR_OK;
 }
 
@@ -136,6 +137,8 @@ int drop_params(float p, uint64_t seed, DropParams* d) {
     const double pd = static_cast<double>(p);
     d->key0 = static_cast<uint32_t>(seed);
     d->key1 = static_cast<uint32_t>(seed >> 32);
+    d->ctr2 = 0u;
+    d->ctr3 = 0u;
     if (p == 1.0f) {
         d->drop_all = 1u;
         d->thr = 0xFFFFFFFFu;
@@ -461,6 +464,8 @@ struct Call {
     Shape s{};
     DropParams drop{};
     bool w_t = false;           // W holds W^T [N, K]
+    // leading dimensions in elements; 0: the dense layout (K for X and W^T, N otherwise)
+    int64_t ldx = 0, ldw = 0, ldr = 0, ldo = 0;
 };
 
 // K step of the tile kernel: 64 when it divides K/P, else 32.  MMAR_FORCE_BK=32 selects
@@ -498,6 +503,10 @@ TileArgs tile_args(const Call& c, int rm0, int rn0, int RM, int RN, int cm, int 
     a.M = c.s.M;
     a.N = c.s.N;
     a.K = c.s.K;
+    a.ldx = c.ldx ? c.ldx : c.s.K;
+    a.ldw = c.ldw ? c.ldw : (c.w_t ? c.s.K : c.s.N);
+    a.ldr = c.ldr ? c.ldr : c.s.N;
+    a.ldo = c.ldo ? c.ldo : c.s.N;
     a.P = c.s.P;
     a.Ks = static_cast<int32_t>(c.s.K / c.s.P);
     a.rm0 = rm0;
@@ -853,8 +862,9 @@ int mmar_fused_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
     const Shape s{M, N, K, P};
     int rc;
     if ((rc = check_shape(s))) return rc;
+    // the residual is read 8 bytes (4 elements) at a time: 8-byte alignment suffices
     if ((rc = check_ptr(X, "X")) || (rc = check_ptr(W, "W")) || (rc = check_ptr(bias, "bias")) ||
-        (rc = check_ptr(residual, "residual")) || (rc = check_ptr(out, "out")))
+        (rc = check_ptr(residual, "residual", 8)) || (rc = check_ptr(out, "out")))
         return rc;
     const size_t ob = static_cast<size_t>(M * N) * 2;
     if (overlaps(out, ob, X, static_cast<size_t>(M * K) * 2) ||
@@ -932,6 +942,64 @@ int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   size_t ws_bytes, void* stream) {
     return fused_impl(X, W, false, bias, residual, out, M, N, K, P, p_drop, seed, schedule,
                       chunk_m, chunk_n, ring, w_mode, tile, workspace, ws_bytes, stream);
+}
+
+int mmar_fused_strided(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                       const uint16_t* bias, const uint16_t* residual, int64_t ldr, float* out,
+                       int64_t ldo, int64_t M, int64_t N, int64_t K, int32_t P, float p_drop,
+                       uint64_t seed, uint64_t philox_offset, void* stream) {
+    g_err.clear();
+    const Shape s{M, N, K, P};
+    int rc;
+    if ((rc = check_shape(s))) return rc;
+    if (ldx < K || ldw < N || ldr < N || ldo < N)
+        return fail(MMAR_EINVAL, "a leading dimension is shorter than its row (ldx >= K, "
+                                 "ldw >= N, ldr >= N, ldo >= N)");
+    if (ldx % 8 != 0 || ldw % 8 != 0)
+        return fail(MMAR_EALIGN, "ldx and ldw must be multiples of 8 elements (16-byte rows)");
+    if (ldr % 4 != 0 || ldo % 4 != 0)
+        return fail(MMAR_EALIGN, "ldr and ldo must be multiples of 4 elements");
+    const int64_t lim = int64_t(1) << 31;
+    const int64_t ex = (M - 1) * ldx + K, ew = (K - 1) * ldw + N, er = (M - 1) * ldr + N,
+                  eo = (M - 1) * ldo + N;
+    if (ldx >= lim || ldw >= lim || ldr >= lim || ldo >= lim || ex >= lim || ew >= lim ||
+        er >= lim || eo >= lim)
+        return fail(MMAR_EINVAL, "every tensor's extent (rows - 1) * ld + row must be below 2^31 "
+                                 "elements");
+    // the residual is read 8 bytes (4 elements) at a time: 8-byte alignment suffices
+    if ((rc = check_ptr(X, "X")) || (rc = check_ptr(W, "W")) || (rc = check_ptr(bias, "bias")) ||
+        (rc = check_ptr(residual, "residual", 8)) || (rc = check_ptr(out, "out")))
+        return rc;
+    const size_t ob = static_cast<size_t>(eo) * 4;
+    if (overlaps(out, ob, X, static_cast<size_t>(ex) * 2) ||
+        overlaps(out, ob, W, static_cast<size_t>(ew) * 2) ||
+        overlaps(out, ob, bias, static_cast<size_t>(N) * 2) ||
+        overlaps(out, ob, residual, static_cast<size_t>(er) * 2))
+        return fail(MMAR_EINVAL, "out overlaps an input");
+    Call c;
+    if ((rc = drop_params(p_drop, seed, &c.drop))) return rc;
+    c.drop.ctr2 = static_cast<uint32_t>(philox_offset);
+    c.drop.ctr3 = static_cast<uint32_t>(philox_offset >> 32);
+    c.X = X;
+    c.W = W;
+    c.bias = bias;
+    c.residual = residual;
+    c.out = out;
+    c.s = s;
+    c.ldx = ldx;
+    c.ldw = ldw;
+    c.ldr = ldr;
+    c.ldo = ldo;
+    DevState* st = nullptr;
+    if ((rc = current_device(&st))) return rc;
+    // the cached plan when it is a persistent one reading W directly, else the default
+    // persistent plan (the other schedules and the pre-transposed weight take dense
+    // buffers)
+    Plan p = plan_for(st, s, MMAR_SCHED_AUTO, 0, 0, 0, MMAR_W_AUTO, MMAR_TILE_AUTO);
+    if (p.sched != MMAR_SCHED_PERSISTENT || p.wmode != MMAR_W_DIRECT)
+        p = plan_for(st, s, MMAR_SCHED_PERSISTENT, 0, 0, 0, MMAR_W_DIRECT, MMAR_TILE_AUTO);
+    return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, static_cast<hipStream_t>(stream),
+                          p.tile);
 }
 
 int mmar_sequential(const uint16_t* X, const uint16_t* W, const uint16_t* bias,

@@ -32,6 +32,7 @@ struct DropParams {
     uint32_t drop_all;  // p == 1: every element is dropped
     float scale;        // fp32(1 / (1 - p)); 1 when p == 0
     uint32_t key0, key1;
+    uint32_t ctr2, ctr3;  // counter words 2 and 3: the low and high word of the offset
 };
 
 // Arguments of the tile kernel.  The kernel covers the output region
@@ -47,6 +48,9 @@ struct TileArgs {
                          // when set
     float* ws;           // kModePartials: [P][RM][RN] for the region
     int64_t M, N, K;
+    // leading dimensions (elements between consecutive rows): X (>= K), W (>= N; >= K for
+    // W^T), residual and out / hout (>= N)
+    int64_t ldx, ldw, ldr, ldo;
     int32_t P, Ks;       // Ks = K / P
     int32_t rm0, rn0, RM, RN;
     int32_t cm, cn;

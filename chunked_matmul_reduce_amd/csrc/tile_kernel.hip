@@ -295,7 +295,7 @@ void tile_kernel(TileArgs a) {
             const int idx = 64 * (C::XQ * wave + q) + lane;
             const int r = idx / C::CPR, pos = idx % C::CPR;
             const int c = pos ^ swz_x<BK>(r);
-            xoff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * a.K + 8 * c) * 2 +
+            xoff[q] = static_cast<uint32_t>((static_cast<int64_t>(min(r, rows - 1)) * a.ldx + 8 * c) * 2 +
                                             copy_bias<TILE, C::XQ>(q));
         }
 #pragma unroll
@@ -305,25 +305,26 @@ void tile_kernel(TileArgs a) {
                 const int r = idx / C::CPR, pos = idx % C::CPR;
                 const int c = pos ^ swz_x<BK>(r);
                 woff[q] = static_cast<uint32_t>(
-                    (static_cast<int64_t>(min(r, cols - 1)) * a.K + 8 * c) * 2 +
+                    (static_cast<int64_t>(min(r, cols - 1)) * a.ldw + 8 * c) * 2 +
                     copy_bias<TILE, C::WQ>(q));
             } else {
                 const int k = idx / (BN / 8), pos = idx % (BN / 8);
                 const int c = pos ^ swz_w<BN>(k);
                 woff[q] = static_cast<uint32_t>(
-                    (static_cast<int64_t>(k) * a.N + min(8 * c, cols - 8)) * 2 +
+                    (static_cast<int64_t>(k) * a.ldw + min(8 * c, cols - 8)) * 2 +
                     copy_bias<TILE, C::WQ>(q));
             }
         }
         const int nsteps = (p_hi - p_lo) * sps;
         const int64_t k_first = static_cast<int64_t>(p_lo) * a.Ks;
         const uint16_t* xbase = static_cast<const uint16_t*>(
-            uniform_ptr(a.X + static_cast<int64_t>(m0) * a.K + k_first));
+            uniform_ptr(a.X + static_cast<int64_t>(m0) * a.ldx + k_first));
         const uint16_t* wbase = static_cast<const uint16_t*>(uniform_ptr(
-            WT ? a.W + static_cast<int64_t>(n0) * a.K + k_first : a.W + k_first * a.N + n0));
-        // bytes per K step; a step's byte offset st * step fits 32 bits (X, W < 2^31 elements)
+            WT ? a.W + static_cast<int64_t>(n0) * a.ldw + k_first : a.W + k_first * a.ldw + n0));
+        // bytes per K step; a step's byte offset st * step fits 32 bits (the extents of X
+        // and W, rows times leading dimension, are below 2^31 elements)
         const uint32_t xstep_b = BK * 2;
-        const uint32_t wstep_b = WT ? BK * 2 : static_cast<uint32_t>(BK * a.N * 2);
+        const uint32_t wstep_b = WT ? BK * 2 : static_cast<uint32_t>(BK * a.ldw * 2);
         // stage of K step st (st >= 0: unsigned arithmetic keeps the modulo short)
         auto xstage = [](int st) { return static_cast<unsigned>(st) % C::XSTAGES; };
         auto wstage = [](int st) { return static_cast<unsigned>(st) % C::WSTAGES; };
@@ -637,7 +638,7 @@ void tile_kernel(TileArgs a) {
             auto issue = [&](auto ic) {   // residual loads of block i (clamped into the tile)
                 constexpr int i = decltype(ic)::value, nb = i / MB, mb = i % MB;
                 const int ml = min(C::RW * wm + 32 * mb, rows - 32) - C::RW * wm;
-                const uint16_t* rp = a.residual + (m_lane + ml) * a.N + n_lane + ncol(nb);
+                const uint16_t* rp = a.residual + (m_lane + ml) * a.ldr + n_lane + ncol(nb);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) rq[i % PF][g] = *reinterpret_cast<const uint2*>(rp + 8 * g);
             };
@@ -660,17 +661,17 @@ void tile_kernel(TileArgs a) {
                     if (ok) {
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const int64_t e = m * a.N + n_lane + 32 * nb + 8 * g;
-                            *reinterpret_cast<float4*>(a.out + e) =
-                                epilogue4(tval(nb, mb, g), bq[g], r0[g], e, a.drop);
+                            const int64_t n = n_lane + 32 * nb + 8 * g;
+                            *reinterpret_cast<float4*>(a.out + m * a.ldo + n) =
+                                epilogue4(tval(nb, mb, g), bq[g], r0[g], m * a.N + n, a.drop);
                         }
                     }
                 } else {   // kModeReduced: T itself
                     if (ok) {
 #pragma unroll
                         for (int g = 0; g < 4; ++g) {
-                            const int64_t e = m * a.N + n_lane + 32 * nb + 8 * g;
-                            *reinterpret_cast<float4*>(a.out + e) = tval(nb, mb, g);
+                            const int64_t n = n_lane + 32 * nb + 8 * g;
+                            *reinterpret_cast<float4*>(a.out + m * a.ldo + n) = tval(nb, mb, g);
                         }
                     }
                 }
@@ -704,7 +705,7 @@ void tile_kernel(TileArgs a) {
                             const float g1 = act(__fadd_rn(acc[4 * g + 1], bf16_hi(b.x)));
                             const float g2 = act(__fadd_rn(acc[4 * g + 2], bf16_lo(b.y)));
                             const float g3 = act(__fadd_rn(acc[4 * g + 3], bf16_hi(b.y)));
-                            *reinterpret_cast<uint2*>(a.hout + m * a.N + n) =
+                            *reinterpret_cast<uint2*>(a.hout + m * a.ldo + n) =
                                 make_uint2(bf16x2_rne(g0, g1), bf16x2_rne(g2, g3));
                         }
             };
@@ -725,7 +726,7 @@ void tile_kernel(TileArgs a) {
                     for (int mb = 0; mb < MB; ++mb) {
                         const int ml = min(C::RW * wm + 32 * mb, rows - 32) + l32;
                         rb[nb][g][mb] = *reinterpret_cast<const uint2*>(
-                            a.residual + (static_cast<int64_t>(m0) + ml) * a.N + n0 + nl);
+                            a.residual + (static_cast<int64_t>(m0) + ml) * a.ldr + n0 + nl);
                     }
                 }
             // the output as fp32, or rounded once more to bf16 (nearest even) when hout is set
@@ -742,17 +743,21 @@ void tile_kernel(TileArgs a) {
                             const f32x16& acc = T[nb][mb];
                             const float4 v = make_float4(acc[4 * g], acc[4 * g + 1],
                                                          acc[4 * g + 2], acc[4 * g + 3]);
-                            const int64_t e = m * a.N + n;
-                            store(e, epilogue4(v, bb[nb][g], rb[nb][g][mb], e, a.drop));
+                            // the counter takes the element's index in the M x N output,
+                            // the address the output's leading dimension
+                            store(m * a.ldo + n, epilogue4(v, bb[nb][g], rb[nb][g][mb],
+                                                           m * a.N + n, a.drop));
                         }
             };
             if (a.hout)
-                store_all([&](int64_t e, float4 o) {
-                    *reinterpret_cast<uint2*>(a.hout + e) =
+                store_all([&](int64_t o_at, float4 o) {
+                    *reinterpret_cast<uint2*>(a.hout + o_at) =
                         make_uint2(bf16x2_rne(o.x, o.y), bf16x2_rne(o.z, o.w));
                 });
             else
-                store_all([&](int64_t e, float4 o) { *reinterpret_cast<float4*>(a.out + e) = o; });
+                store_all([&](int64_t o_at, float4 o) {
+                    *reinterpret_cast<float4*>(a.out + o_at) = o;
+                });
         } else if constexpr (MODE == kModePartials) {
             // The slice partial S_p through the idle copy ring to whole-row stores: each
             // wave writes its 64 x 128 block into its own 32 KB (16-byte chunk c of row r at
@@ -797,7 +802,7 @@ void tile_kernel(TileArgs a) {
                         const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
                         const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
                         const f32x16& acc = T[nb][mb];
-                        *reinterpret_cast<float4*>(a.out + m * a.N + n) = make_float4(
+                        *reinterpret_cast<float4*>(a.out + m * a.ldo + n) = make_float4(
                             acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
                     }
         }

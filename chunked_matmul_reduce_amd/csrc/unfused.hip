@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void dropout_kernel(float* V, uint8_t* mask, i
     for (int64_t q = blockIdx.x * 256ll + threadIdx.x; q < groups; q += gridDim.x * 256ll) {
         const uint64_t g = static_cast<uint64_t>(q);   // group of linear elements 4q .. 4q+3
         const uint4 w = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32),
-                                      0u, 0u, d.key0, d.key1);
+                                      d.ctr2, d.ctr3, d.key0, d.key1);
         const bool k0 = !d.drop_all && w.x >= d.thr, k1 = !d.drop_all && w.y >= d.thr;
         const bool k2 = !d.drop_all && w.z >= d.thr, k3 = !d.drop_all && w.w >= d.thr;
         float4 v = reinterpret_cast<float4*>(V)[q];

@@ -175,6 +175,26 @@ int mmar_fused_ex(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
                   int32_t chunk_n, int32_t ring, int32_t w_mode, int32_t tile, void* workspace,
                   size_t ws_bytes, void* stream);
 
+/* The fused block (the CoCoNet record LIT-735, "Key takeaways", second bullet) over
+ * buffers with leading dimensions and a dropout stream offset.  ldx, ldw, ldr, ldo: elements
+ * between consecutive rows of X [M,K], W [K,N], residual [M,N] and out [M,N] (each at
+ * least its row length; ldx and ldw multiples of 8, ldr and ldo multiples of 4; every
+ * extent (rows - 1) * ld + row below 2^31 elements), so that a rank's operand can be a view
+ * into a larger buffer, as the K-slice X[:, K_p] of the shard view is a column block of X
+ * with leading dimension K.  philox_offset fills counter words 2 and 3 (low, high 32 bits)
+ * of the mask's Philox blocks, which every other entry point leaves 0: element (m, n) takes
+ * word e & 3 of the block with counter (lo32(e>>2), hi32(e>>2), lo32(offset), hi32(offset)),
+ * e = m*N + n whatever the leading dimensions, so one seed gives an independent mask per
+ * offset (a layer or step index) and offset 0 reproduces mmar_fused's bits.  Runs the
+ * persistent schedule (the cached plan if it is a persistent one reading W directly, else
+ * the default persistent plan); needs no workspace and allocates nothing.  The residual
+ * pointer needs 8-byte alignment only (the others 16).  Preconditions, dropout and errors
+ * otherwise as mmar_fused; out must not overlap any input's extent. */
+int mmar_fused_strided(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                       const uint16_t* bias, const uint16_t* residual, int64_t ldr, float* out,
+                       int64_t ldo, int64_t M, int64_t N, int64_t K, int32_t P, float p_drop,
+                       uint64_t seed, uint64_t philox_offset, void* stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): mmar_fused_ex with its workspace taken
  * from a static per-device array of mmar_noalloc_workspace_capacity() bytes (64 MiB) that

@@ -19,9 +19,11 @@ print no numeric example, so each choice they leave open is a stated reading:
 * dropout is inverted dropout: a kept value is multiplied by 1/(1-p), a dropped one
   contributes zero;
 * the keep decision for the element at row m, column n uses e = m*N + n: the
-  Philox4x32-10 block with counter (lo32(e>>2), hi32(e>>2), 0, 0) and key
-  (lo32(seed), hi32(seed)); r = word (e & 3) of that block; the element is dropped iff
-  r < floor(p * 2^32), with p taken as an fp32 value; p = 1 drops everything;
+  Philox4x32-10 block with counter (lo32(e>>2), hi32(e>>2), lo32(offset), hi32(offset))
+  and key (lo32(seed), hi32(seed)); r = word (e & 3) of that block; the element is
+  dropped iff r < floor(p * 2^32), with p taken as an fp32 value; p = 1 drops
+  everything.  The offset (counter words 2 and 3) is 0 unless a caller asks for a
+  separate stream under the same seed (a layer or step index);
 * p outside [0, 1] or not finite is an error.
 
 Everything here is fp64 except the keep decision (integer) and ``reduce_epilogue_fp32``,
@@ -74,8 +76,9 @@ def keep_scale(p_drop) -> float:
 
 
 # ---------------------------------------------------------------- mask
-def keep_elements(e, p_drop, seed) -> np.ndarray:
-    """Keep decision for linear output indices ``e`` (int64 array, e = m*N + n)."""
+def keep_elements(e, p_drop, seed, offset=0) -> np.ndarray:
+    """Keep decision for linear output indices ``e`` (int64 array, e = m*N + n); ``offset``
+    fills Philox counter words 2 and 3."""
     e = np.asarray(e, dtype=np.uint64)
     thr = drop_threshold(p_drop)
     if thr >= _TWO32:
@@ -83,15 +86,17 @@ def keep_elements(e, p_drop, seed) -> np.ndarray:
     g = e >> np.uint64(2)
     word = (e & np.uint64(3)).astype(np.intp)
     seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+    off = int(offset) & 0xFFFFFFFFFFFFFFFF
     blk = philox.blocks_np((g & np.uint64(0xFFFFFFFF)).astype(np.uint32).ravel(),
-                           (g >> np.uint64(32)).astype(np.uint32).ravel(), 0, 0,
-                           seed & 0xFFFFFFFF, seed >> 32)
+                           (g >> np.uint64(32)).astype(np.uint32).ravel(),
+                           off & 0xFFFFFFFF, off >> 32, seed & 0xFFFFFFFF, seed >> 32)
     r = blk[np.arange(blk.shape[0]), word.ravel()].reshape(e.shape)
     return r.astype(np.int64) >= thr
 
 
-def keep_mask(M, N, p_drop, seed, rows=None) -> np.ndarray:
-    """Keep mask of the [M, N] output (or of the listed rows only), bool."""
+def keep_mask(M, N, p_drop, seed, rows=None, offset=0) -> np.ndarray:
+    """Keep mask of the [M, N] output (or of the listed rows only), bool; ``offset`` fills
+    Philox counter words 2 and 3."""
     thr = drop_threshold(p_drop)
     rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
     if thr >= _TWO32:
@@ -101,12 +106,13 @@ def keep_mask(M, N, p_drop, seed, rows=None) -> np.ndarray:
         G = (M * N) // 4
         g = np.arange(G, dtype=np.uint64)
         seed = int(seed) & 0xFFFFFFFFFFFFFFFF
+        off = int(offset) & 0xFFFFFFFFFFFFFFFF
         blk = philox.blocks_np((g & np.uint64(0xFFFFFFFF)).astype(np.uint32),
-                               (g >> np.uint64(32)).astype(np.uint32), 0, 0,
-                               seed & 0xFFFFFFFF, seed >> 32)
+                               (g >> np.uint64(32)).astype(np.uint32),
+                               off & 0xFFFFFFFF, off >> 32, seed & 0xFFFFFFFF, seed >> 32)
         return (blk.reshape(M, N).astype(np.int64) >= thr)
     e = rows[:, None].astype(np.int64) * N + np.arange(N, dtype=np.int64)[None, :]
-    return keep_elements(e, p_drop, seed)
+    return keep_elements(e, p_drop, seed, offset)
 
 
 # ---------------------------------------------------------------- the block
@@ -130,8 +136,9 @@ def slice_partials(X_bits, W_bits, P, rows=None, cols=None):
         yield widen(Xp) @ widen(Wp)
 
 
-def run(X, W, bias, residual, P, p_drop, seed, rows=None, cols=None):
-    """The block in fp64.  Returns (out [M,N] fp64, keep [M,N] bool).
+def run(X, W, bias, residual, P, p_drop, seed, rows=None, cols=None, offset=0):
+    """The block in fp64.  Returns (out [M,N] fp64, keep [M,N] bool).  ``offset``: Philox
+    counter words 2 and 3 of the mask.
 
     ``rows`` / ``cols`` restrict the computation to a sub-grid of the output (every
     output element depends only on its own row of X and column of W); the mask still
@@ -148,10 +155,10 @@ def run(X, W, bias, residual, P, p_drop, seed, rows=None, cols=None):
     rr = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
     cc = np.arange(N) if cols is None else np.asarray(cols, dtype=np.int64)
     if cols is None:
-        keep = keep_mask(M, N, p_drop, seed, rows=None if rows is None else rr)
+        keep = keep_mask(M, N, p_drop, seed, rows=None if rows is None else rr, offset=offset)
     else:
         e = rr[:, None] * N + cc[None, :]
-        keep = keep_elements(e, p_drop, seed)
+        keep = keep_elements(e, p_drop, seed, offset)
     res = np.asarray(residual)
     res = res if rows is None else res[rr]
     res = res if cols is None else res[:, cc]
@@ -192,9 +199,10 @@ def error_bound_fp32(X, W, bias, residual, P, p_drop, keep, rows=None, cols=None
 
 
 def run_inputs(inp, rows=None, cols=None):
-    """``run`` on a dict with keys X, W, bias, residual, P, p_drop, seed."""
+    """``run`` on a dict with keys X, W, bias, residual, P, p_drop, seed (and optionally
+    offset)."""
     return run(inp["X"], inp["W"], inp["bias"], inp["residual"], inp["P"], inp["p_drop"],
-               inp["seed"], rows=rows, cols=cols)
+               inp["seed"], rows=rows, cols=cols, offset=inp.get("offset", 0))
 
 
 # ---------------------------------------------------------------- fp32 order model

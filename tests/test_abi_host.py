@@ -154,3 +154,36 @@ def test_no_device_reports_enodev():
     assert _fused() == mmar.ENODEV
     assert mmar.lib.mmar_autotune(64, 256, 256, 4, 0) == mmar.ENODEV
     assert mmar.lib.mmar_release() == mmar.OK
+
+
+def _strided(**kw):
+    a = dict(X=FAKE, ldx=256, W=FAKE * 2, ldw=256, bias=FAKE * 3, res=FAKE * 4, ldr=256,
+             out=FAKE * 64, ldo=256, M=64, N=256, K=256, P=4, p=0.1, seed=0, off=0)
+    a.update(kw)
+    return mmar.lib.mmar_fused_strided(a["X"], a["ldx"], a["W"], a["ldw"], a["bias"], a["res"],
+                                       a["ldr"], a["out"], a["ldo"], a["M"], a["N"], a["K"],
+                                       a["P"], a["p"], a["seed"], a["off"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(ldx=224), mmar.EINVAL, "leading dimension"), (dict(ldw=200), mmar.EINVAL, "leading"),
+    (dict(ldr=128), mmar.EINVAL, "leading"), (dict(ldo=252), mmar.EINVAL, "leading"),
+    (dict(ldx=260), mmar.EALIGN, "ldx and ldw"), (dict(ldw=268), mmar.EALIGN, "ldx and ldw"),
+    (dict(ldr=258), mmar.EALIGN, "ldr and ldo"), (dict(ldo=262), mmar.EALIGN, "ldr and ldo"),
+    (dict(ldx=1 << 26), mmar.EINVAL, "2^31"), (dict(X=None), mmar.EINVAL, "X is NULL"),
+    (dict(out=FAKE * 2), mmar.EINVAL, "overlaps"), (dict(P=3), mmar.EINVAL, "P must divide K"),
+    (dict(p=1.5), mmar.EINVAL, "p_drop"), (dict(res=FAKE * 4 + 4), mmar.EALIGN, "residual"),
+    (dict(W=FAKE * 2 + 8), mmar.EALIGN, "W is not 16-byte"),
+    # out's extent with a long row stride reaches the residual at FAKE * 4 + ...
+    (dict(out=FAKE * 3 + 1024, ldo=8192), mmar.EINVAL, "overlaps"),
+])
+def test_strided_entry_validates_before_device(kw, code, msg):
+    assert _strided(**kw) == code
+    assert msg in mmar.last_error()
+
+
+def test_strided_entry_without_device():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; the no-device path is for CPU-only hosts")
+    assert _strided(ldx=264, ldw=320, ldr=260, ldo=300, off=2 ** 64 - 1) == mmar.ENODEV

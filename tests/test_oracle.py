@@ -217,6 +217,42 @@ def test_mask_matches_scalar_philox_per_element():
         assert keep[m, n] == (w >= thr)
 
 
+@pytest.mark.parametrize("offset", [1, 0xFFFFFFFF, 2 ** 32, 0x0123456789ABCDEF, 2 ** 64 - 1])
+def test_mask_with_offset_matches_scalar_philox_per_element(offset):
+    """A non-zero stream offset fills counter words 2 (low half) and 3 (high half)."""
+    M, N, seed, p = 64, 96, 0x5EED, np.float32(0.3)
+    keep = oracle.keep_mask(M, N, p, seed, offset=offset)
+    thr = oracle.drop_threshold(p)
+    rng = np.random.default_rng(5)
+    for m, n in zip(rng.integers(0, M, 300), rng.integers(0, N, 300)):
+        e = int(m) * N + int(n)
+        w = philox.block_scalar((e >> 2, 0, offset & 0xFFFFFFFF, offset >> 32),
+                                (seed & 0xFFFFFFFF, seed >> 32))[e & 3]
+        assert keep[m, n] == (w >= thr)
+    # the row-subset and element paths agree with the whole-output path
+    rows = np.array([3, 0, 63])
+    assert np.array_equal(oracle.keep_mask(M, N, p, seed, rows=rows, offset=offset), keep[rows])
+    e = np.arange(M * N).reshape(M, N)
+    assert np.array_equal(oracle.keep_elements(e, p, seed, offset), keep)
+
+
+def test_offset_zero_is_the_default_and_offsets_give_independent_masks():
+    a = oracle.keep_mask(128, 256, 0.1, 9)
+    assert np.array_equal(oracle.keep_mask(128, 256, 0.1, 9, offset=0), a)
+    for off in (1, 2 ** 32):
+        b = oracle.keep_mask(128, 256, 0.1, 9, offset=off)
+        assert abs((a != b).mean() - 2 * 0.1 * 0.9) < 0.02
+    # run() threads the offset to the mask: dropped elements equal the residual exactly
+    inp = make_random_inputs(32, 64, 32, 2)
+    X, W, bias, res = inp["X"], inp["W"], inp["bias"], inp["residual"]
+    out0, k0 = oracle.run(X, W, bias, res, 2, 0.5, 3)
+    out1, k1 = oracle.run(X, W, bias, res, 2, 0.5, 3, offset=7)
+    assert np.array_equal(k1, oracle.keep_mask(32, 32, 0.5, 3, offset=7))
+    assert not np.array_equal(k0, k1)
+    assert np.array_equal(out1[~k1], oracle.widen(res)[~k1])
+    assert np.array_equal(out1[k1 & k0], out0[k1 & k0])
+
+
 def test_mask_row_subsets_and_elements_agree():
     M, N = 64, 96
     full = oracle.keep_mask(M, N, 0.1, 77)

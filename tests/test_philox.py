@@ -61,17 +61,30 @@ def test_known_answers_against_rocrand(tmp_path_factory):
              (4, 6_291_455), (3, 2 ** 33 + 17)]
     pairs += [(int(s), int(g)) for s, g in zip(rng.integers(0, 2 ** 63, 500, dtype=np.uint64),
                                                rng.integers(0, 2 ** 61, 500, dtype=np.uint64))]
-    text = "".join(f"{s} {g}\n" for s, g in pairs)
+    text = "".join(f"{s} {g} 0\n" for s, g in pairs)
     r = subprocess.run([exe], input=text, capture_output=True, text=True, check=True)
     lines = r.stdout.split("\n")
     for (s, g), line in zip(pairs, lines):
         want = tuple(int(w, 16) for w in line.split())
         got = philox.block_scalar((g & 0xFFFFFFFF, g >> 32, 0, 0), (s & 0xFFFFFFFF, s >> 32))
         assert got == want, (s, g)
+    # non-zero counter words 2 and 3 (rocRAND's subsequence): the mask's stream offset
+    trip = [(0, 0, 1), (5, 3, 2 ** 32), (2 ** 64 - 1, 2 ** 40 + 3, 2 ** 64 - 1),
+            (0x5EED, 17, 0x0123456789ABCDEF)]
+    trip += [(int(s), int(g), int(o)) for s, g, o in zip(rng.integers(0, 2 ** 63, 300, dtype=np.uint64),
+                                                         rng.integers(0, 2 ** 61, 300, dtype=np.uint64),
+                                                         rng.integers(0, 2 ** 63, 300, dtype=np.uint64))]
+    r = subprocess.run([exe], input="".join(f"{s} {g} {o}\n" for s, g, o in trip),
+                       capture_output=True, text=True, check=True)
+    for (s, g, o), line in zip(trip, r.stdout.split("\n")):
+        want = tuple(int(w, 16) for w in line.split())
+        got = philox.block_scalar((g & 0xFFFFFFFF, g >> 32, o & 0xFFFFFFFF, o >> 32),
+                                  (s & 0xFFFFFFFF, s >> 32))
+        assert got == want, (s, g, o)
     # the vectorized form over a contiguous run of counters, seed 2
     g = np.arange(4096, dtype=np.uint64)
     vec = philox.blocks_np(g.astype(np.uint32), 0, 0, 0, 2, 0)
-    r = subprocess.run([exe], input="".join(f"2 {i}\n" for i in range(4096)),
+    r = subprocess.run([exe], input="".join(f"2 {i} 0\n" for i in range(4096)),
                        capture_output=True, text=True, check=True)
     want = np.array([[int(w, 16) for w in ln.split()] for ln in r.stdout.strip().split("\n")],
                     dtype=np.uint32)
