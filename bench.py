@@ -37,6 +37,8 @@ its first launches; the timed steps then run at the sustained clock.
 --only copy      one plain 1 GiB device copy, the calibration point for HBM counters
 --only vendor    time only hipBLASLt's plain bf16 GEMM at the block's shape (torch.matmul),
                  the vendor yardstick, for its kernel trace
+--only tune      autotune the four block workloads and print the plans chosen (with
+                 MMAR_PLAN_CACHE set, the cache file also records each plan's margin)
 """
 import argparse
 import hashlib
@@ -197,7 +199,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gpt2_mlp")
-    ap.add_argument("--only", choices=["all", "fused", "streams", "producer", "copy", "vendor"],
+    ap.add_argument("--only", choices=["all", "fused", "streams", "producer", "copy", "vendor",
+                                       "tune"],
                     default="all")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -228,6 +231,15 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n}))
+        return
+
+    if args.only == "tune":
+        plans = {}
+        for name in ("gpt2_attn", "gpt2_mlp", "bert_mlp", "gpt3_mlp"):
+            wl = WORKLOADS[name]
+            mmar.autotune(wl.M, wl.N, wl.K, wl.P)
+            plans[name] = mmar.get_plan(wl.M, wl.N, wl.K, wl.P)
+        print(json.dumps({"only": "tune", "plans": plans}), flush=True)
         return
 
     w = WORKLOADS[args.workload]

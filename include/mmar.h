@@ -318,11 +318,14 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
 
 /* The autotuner (CoCoNet picks its schedules by automatic search; "Key takeaways", first
  * bullet): times candidate {schedule, tile, chunk, weight mode} plans for this shape on
- * library-owned buffers, 25 rounds interleaved (each round runs every candidate once), and
- * keeps the default plan unless a candidate's median time beats it by more than the
- * larger of the two interquartile ranges; the best such candidate goes to the plan cache
- * (also written, with that margin, to the JSON file named by the MMAR_PLAN_CACHE
- * environment variable, if set).  flags: bit 0 = also try MMAR_SCHED_STREAMS and
+ * library-owned buffers, 25 rounds interleaved (each round runs every candidate once, in
+ * an order rotated from round to round), and keeps the default plan unless a candidate's
+ * median time beats it by more than the larger of the two interquartile ranges and by at
+ * least 1 % of the default's median; among such candidates the fastest wins, and a
+ * candidate tied with it within their interquartile ranges wins instead if it comes
+ * first in candidate order (larger chunks, W read directly, the 256 x 128 tile).  The
+ * choice goes to the plan cache (also written, with its margin, to the JSON file named by
+ * the MMAR_PLAN_CACHE environment variable, if set).  flags: bit 0 = also try MMAR_SCHED_STREAMS and
  * MMAR_SCHED_SEQUENTIAL plans.  Synchronizes the device. */
 int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags);
 
