@@ -317,6 +317,29 @@ void tile_kernel(TileArgs a) {
         }
         const int nsteps = (p_hi - p_lo) * sps;
         const int64_t k_first = static_cast<int64_t>(p_lo) * a.Ks;
+
+        // The fused epilogue's residual tile through the X ring.  On a full tile whose
+        // residual rows are 16-byte aligned, the last two K steps (whose copies would only
+        // repeat the last step's operands) copy residual rows 0-127 and 128-255 into the
+        // X stages they free, 16 chunks of 16 bytes per row, chunk c of row r at slot
+        // c ^ (r mod 16) (so the epilogue's reads of 32 rows spread over the banks); the
+        // epilogue then reads the residual from LDS instead of waiting for HBM at the end
+        // of every round.
+        constexpr bool RES_OK = MODE == kModeFused && TILE == kTile128 && C::LEAD == 2 &&
+                                C::XQ == 4 && C::NW == 8 && BN == 128;
+        bool use_res = false;
+        uint32_t roff[RES_OK ? C::XQ : 1];
+        if constexpr (RES_OK) {
+            use_res = rows == BM && cols == BN && sps >= 3 && a.hout == nullptr &&
+                      (reinterpret_cast<uintptr_t>(a.residual) % 16) == 0 && (a.ldr % 8) == 0;
+#pragma unroll
+            for (int q = 0; q < C::XQ; ++q) {   // slot 64 (XQ w + q) + lane of a 128-row half
+                const int idx = 64 * (C::XQ * wave + q) + lane;
+                const int r = idx >> 4, c = (idx & 15) ^ (r & 15);
+                roff[q] = static_cast<uint32_t>(r * static_cast<uint32_t>(a.ldr) * 2u + 16u * c) +
+                          copy_bias<TILE, C::XQ>(q);
+            }
+        }
         const uint16_t* xbase = static_cast<const uint16_t*>(
             uniform_ptr(a.X + static_cast<int64_t>(m0) * a.ldx + k_first));
         const uint16_t* wbase = static_cast<const uint16_t*>(uniform_ptr(
@@ -333,14 +356,40 @@ void tile_kernel(TileArgs a) {
                                                      static_cast<uint32_t>(st) * step_b);
         };
 
-        // copy operation j of step st: X copies 2j, 2j+1 (j < XOPS), else W copies q, q+1
-        // (q = 2 (j - XOPS)), or W copy q alone when it is the last of an odd count
+        // The X copies' source, destination step and per-lane offsets for the current K
+        // step (set by x_copies_for): step st's X operands, or, in the last two K steps of
+        // a tile whose residual goes through LDS, residual rows 128 half .. +127 into the X
+        // stage of step cur + LEAD, instead of a repeat of the last step's X operands
+        // (selects, not branches, so the copy pattern stays one basic block).
+        const uint16_t* xsrc_cur = xbase;
+        int xdst_cur = 0;
+        uint32_t xo_cur[C::XQ];
+        auto x_copies_for = [&](int st, int cur) {
+            xsrc_cur = step_ptr(xbase, st, xstep_b);
+            xdst_cur = st;
+#pragma unroll
+            for (int q = 0; q < C::XQ; ++q) xo_cur[q] = xoff[q];
+            if constexpr (RES_OK) {
+                const bool rs = use_res && cur + C::LEAD >= nsteps;
+                const int half = cur + C::LEAD - nsteps;
+                if (rs) {
+                    xsrc_cur = static_cast<const uint16_t*>(uniform_ptr(
+                        a.residual + (static_cast<int64_t>(m0) + 128 * half) * a.ldr + n0));
+                    xdst_cur = cur + C::LEAD;
+                }
+#pragma unroll
+                for (int q = 0; q < C::XQ; ++q) xo_cur[q] = rs ? roff[q] : xoff[q];
+            }
+        };
+        // copy operation j of step st: X copies 2j, 2j+1 (j < XOPS; from x_copies_for), else
+        // W copies q, q+1 (q = 2 (j - XOPS)), or W copy q alone when it is the last of an
+        // odd count
         auto copy_op = [&](int st, int j) {
             if (j < C::XOPS) {
                 const int i = 2 * j;
-                const uint32_t xd = lds_addr(xs_base + xstage(st) * C::XS +
+                const uint32_t xd = lds_addr(xs_base + xstage(xdst_cur) * C::XS +
                                              (C::XQ * uwave + i + 1) * 512);
-                dma16x2(step_ptr(xbase, st, xstep_b), xoff[i], xoff[i + 1], xd);
+                dma16x2(xsrc_cur, xo_cur[i], xo_cur[i + 1], xd);
             } else {
                 const int q = 2 * (j - C::XOPS);
                 if (q + 1 < C::WQ) {
@@ -409,9 +458,11 @@ void tile_kernel(TileArgs a) {
         };
 
 #pragma unroll
-        for (int d = 0; d < C::LEAD; ++d)
+        for (int d = 0; d < C::LEAD; ++d) {
+            x_copies_for(min(d, last), d - C::LEAD);
 #pragma unroll
             for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), j);
+        }
         handshake();
 
         // running-total blocks (nb = NB - 1, mb < TLDS) kept in this wave's LDS area (the
@@ -545,8 +596,10 @@ void tile_kernel(TileArgs a) {
         auto kstep = [&](auto zero_tag) {
             constexpr bool ZERO = decltype(zero_tag)::value;
             // copies of step st+LEAD (the last steps re-copy the last one: identical bytes,
-            // no branch), spread over the MFMAs of k steps 0 .. KS-2
+            // no branch, except that the X copies carry the residual when it goes through
+            // LDS), spread over the MFMAs of k steps 0 .. KS-2
             const int st2 = min(st + C::LEAD, last);
+            x_copies_for(st2, st);
             // the NB x MB MFMAs of one k step, with copy operations c0 .. c1-1 issued between
             // them (all of them: the caller passes c1 - c0 <= OPS)
             auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1,
@@ -714,7 +767,7 @@ void tile_kernel(TileArgs a) {
             else
                 store_all([](float v) { return v; });
         } else if constexpr (MODE == kModeFused) {
-            uint2 bb[NB][4], rb[NB][4][MB];
+            uint2 bb[NB][4];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -722,15 +775,10 @@ void tile_kernel(TileArgs a) {
                     // clamped into the tile: an outside block reads a valid address
                     const int nl = min(C::CW * wn + 32 * nb, cols - 32) + 8 * g + 4 * h;
                     bb[nb][g] = *reinterpret_cast<const uint2*>(a.bias + n0 + nl);
-#pragma unroll
-                    for (int mb = 0; mb < MB; ++mb) {
-                        const int ml = min(C::RW * wm + 32 * mb, rows - 32) + l32;
-                        rb[nb][g][mb] = *reinterpret_cast<const uint2*>(
-                            a.residual + (static_cast<int64_t>(m0) + ml) * a.ldr + n0 + nl);
-                    }
                 }
-            // the output as fp32, or rounded once more to bf16 (nearest even) when hout is set
-            auto store_all = [&](auto store) {
+            // the output as fp32, or rounded once more to bf16 (nearest even) when hout is
+            // set; res(nb, g, mb) gives the residual of the lane's group
+            auto store_all = [&](auto store, auto res) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -745,19 +793,53 @@ void tile_kernel(TileArgs a) {
                                                          acc[4 * g + 2], acc[4 * g + 3]);
                             // the counter takes the element's index in the M x N output,
                             // the address the output's leading dimension
-                            store(m * a.ldo + n, epilogue4(v, bb[nb][g], rb[nb][g][mb],
+                            store(m * a.ldo + n, epilogue4(v, bb[nb][g], res(nb, g, mb),
                                                            m * a.N + n, a.drop));
                         }
             };
-            if (a.hout)
-                store_all([&](int64_t o_at, float4 o) {
-                    *reinterpret_cast<uint2*>(a.hout + o_at) =
-                        make_uint2(bf16x2_rne(o.x, o.y), bf16x2_rne(o.z, o.w));
-                });
-            else
-                store_all([&](int64_t o_at, float4 o) {
-                    *reinterpret_cast<float4*>(a.out + o_at) = o;
-                });
+            auto store_f32 = [&](int64_t o_at, float4 o) {
+                *reinterpret_cast<float4*>(a.out + o_at) = o;
+            };
+            if (RES_OK && use_res) {
+                // the residual from the ring, read next to its use (an LDS read, no load
+                // latency to hide); full tile: row r, columns nl .. nl + 3 = chunk nl / 8,
+                // half h
+                auto res_lds = [&](int nb, int g, int mb) -> uint2 {
+                    const int r = C::RW * wm + 32 * mb + l32, rr = r & 127;
+                    const int nl = C::CW * wn + 32 * nb + 8 * g + 4 * h;
+                    const int slot = rr * 16 + ((nl >> 3) ^ (rr & 15));
+                    return *reinterpret_cast<const uint2*>(xs_base + xstage(last + 1 + (r >> 7)) * C::XS +
+                                                           slot * 8 + (nl & 7));
+                };
+                store_all(store_f32, res_lds);
+                // every wave has read its residual from the ring before the next item's
+                // copies refill it
+                wg_barrier();
+            } else {
+                // every residual load issued first, so they are in flight together (and
+                // under the Philox arithmetic) instead of one load latency per group
+                uint2 rb[NB][4][MB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int nl = min(C::CW * wn + 32 * nb, cols - 32) + 8 * g + 4 * h;
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            const int ml = min(C::RW * wm + 32 * mb, rows - 32) + l32;
+                            rb[nb][g][mb] = *reinterpret_cast<const uint2*>(
+                                a.residual + (static_cast<int64_t>(m0) + ml) * a.ldr + n0 + nl);
+                        }
+                    }
+                auto res_reg = [&](int nb, int g, int mb) { return rb[nb][g][mb]; };
+                if (a.hout)
+                    store_all([&](int64_t o_at, float4 o) {
+                        *reinterpret_cast<uint2*>(a.hout + o_at) =
+                            make_uint2(bf16x2_rne(o.x, o.y), bf16x2_rne(o.z, o.w));
+                    }, res_reg);
+                else
+                    store_all(store_f32, res_reg);
+            }
         } else if constexpr (MODE == kModePartials) {
             // The slice partial S_p through the idle copy ring to whole-row stores: each
             // wave writes its 64 x 128 block into its own 32 KB (16-byte chunk c of row r at
