@@ -356,40 +356,24 @@ void tile_kernel(TileArgs a) {
                                                      static_cast<uint32_t>(st) * step_b);
         };
 
-        // The X copies' source, destination step and per-lane offsets for the current K
-        // step (set by x_copies_for): step st's X operands, or, in the last two K steps of
-        // a tile whose residual goes through LDS, residual rows 128 half .. +127 into the X
-        // stage of step cur + LEAD, instead of a repeat of the last step's X operands
-        // (selects, not branches, so the copy pattern stays one basic block).
-        const uint16_t* xsrc_cur = xbase;
-        int xdst_cur = 0;
-        uint32_t xo_cur[C::XQ];
-        auto x_copies_for = [&](int st, int cur) {
-            xsrc_cur = step_ptr(xbase, st, xstep_b);
-            xdst_cur = st;
-#pragma unroll
-            for (int q = 0; q < C::XQ; ++q) xo_cur[q] = xoff[q];
-            if constexpr (RES_OK) {
-                const bool rs = use_res && cur + C::LEAD >= nsteps;
-                const int half = cur + C::LEAD - nsteps;
-                if (rs) {
-                    xsrc_cur = static_cast<const uint16_t*>(uniform_ptr(
-                        a.residual + (static_cast<int64_t>(m0) + 128 * half) * a.ldr + n0));
-                    xdst_cur = cur + C::LEAD;
-                }
-#pragma unroll
-                for (int q = 0; q < C::XQ; ++q) xo_cur[q] = rs ? roff[q] : xoff[q];
-            }
+        // residual copy pair j (j < XOPS) issued during K step cur, one of the last two
+        // (cur = nsteps - 2 + half): residual rows 128 half .. +127 into the X stage of step
+        // cur + LEAD, which the repeat of the last step's X operands would have filled
+        auto res_copy_op = [&](int j, int cur) {
+            const int i = 2 * j, half = cur + C::LEAD - nsteps;
+            const uint32_t xd = lds_addr(xs_base + xstage(cur + C::LEAD) * C::XS +
+                                         (C::XQ * uwave + i + 1) * 512);
+            dma16x2(uniform_ptr(a.residual + (static_cast<int64_t>(m0) + 128 * half) * a.ldr + n0),
+                    roff[i], roff[i + 1], xd);
         };
-        // copy operation j of step st: X copies 2j, 2j+1 (j < XOPS; from x_copies_for), else
-        // W copies q, q+1 (q = 2 (j - XOPS)), or W copy q alone when it is the last of an
-        // odd count
+        // copy operation j of step st: X copies 2j, 2j+1 (j < XOPS), else W copies q, q+1
+        // (q = 2 (j - XOPS)), or W copy q alone when it is the last of an odd count
         auto copy_op = [&](int st, int j) {
             if (j < C::XOPS) {
                 const int i = 2 * j;
-                const uint32_t xd = lds_addr(xs_base + xstage(xdst_cur) * C::XS +
+                const uint32_t xd = lds_addr(xs_base + xstage(st) * C::XS +
                                              (C::XQ * uwave + i + 1) * 512);
-                dma16x2(xsrc_cur, xo_cur[i], xo_cur[i + 1], xd);
+                dma16x2(step_ptr(xbase, st, xstep_b), xoff[i], xoff[i + 1], xd);
             } else {
                 const int q = 2 * (j - C::XOPS);
                 if (q + 1 < C::WQ) {
@@ -458,11 +442,9 @@ void tile_kernel(TileArgs a) {
         };
 
 #pragma unroll
-        for (int d = 0; d < C::LEAD; ++d) {
-            x_copies_for(min(d, last), d - C::LEAD);
+        for (int d = 0; d < C::LEAD; ++d)
 #pragma unroll
             for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), j);
-        }
         handshake();
 
         // running-total blocks (nb = NB - 1, mb < TLDS) kept in this wave's LDS area (the
@@ -593,13 +575,14 @@ void tile_kernel(TileArgs a) {
         // them, the step-boundary handshake before the last k step.  ZERO marks the first
         // K step of a slice: its first k step gives the MFMAs a zero accumulator input,
         // which starts the slice sums from zero without clearing any register.
-        auto kstep = [&](auto zero_tag) {
+        auto kstep = [&](auto zero_tag, auto res_tag) {
             constexpr bool ZERO = decltype(zero_tag)::value;
+            // RES: one of the last two K steps of a tile whose residual goes through LDS;
+            // its X copy slots carry residual copies (the same number of copies per step)
+            constexpr bool RES = decltype(res_tag)::value;
             // copies of step st+LEAD (the last steps re-copy the last one: identical bytes,
-            // no branch, except that the X copies carry the residual when it goes through
-            // LDS), spread over the MFMAs of k steps 0 .. KS-2
+            // no branch), spread over the MFMAs of k steps 0 .. KS-2
             const int st2 = min(st + C::LEAD, last);
-            x_copies_for(st2, st);
             // the NB x MB MFMAs of one k step, with copy operations c0 .. c1-1 issued between
             // them (all of them: the caller passes c1 - c0 <= OPS)
             auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1,
@@ -616,7 +599,14 @@ void tile_kernel(TileArgs a) {
                             c0 + ((nb * MB + mb + 1) * (c1 - c0) + NB * MB - 1) / (NB * MB);
                         while (c < upto) {
                             __builtin_amdgcn_sched_barrier(0);
-                            copy_op(st2, c);
+                            if constexpr (RES) {
+                                if (c < C::XOPS)
+                                    res_copy_op(c, st);
+                                else
+                                    copy_op(st2, c);
+                            } else {
+                                copy_op(st2, c);
+                            }
                             c += 1;
                             __builtin_amdgcn_sched_barrier(0);
                         }
@@ -641,10 +631,22 @@ void tile_kernel(TileArgs a) {
             }
         };
 
+        // the slices' K steps; with the residual through LDS the last two steps of the
+        // last slice are the residual variant (peeled after one loop with a shorter bound)
         for (int p = p_lo; p < p_hi; ++p) {
-          kstep(std::true_type{});
+          const bool peel = RES_OK && use_res && p == p_hi - 1;
+          kstep(std::true_type{}, std::false_type{});
           ++st;
-          for (int j = 1; j < sps; ++j, ++st) kstep(std::false_type{});
+          const int jend = peel ? sps - 2 : sps;
+          for (int j = 1; j < jend; ++j, ++st) kstep(std::false_type{}, std::false_type{});
+          if constexpr (RES_OK) {
+              if (peel) {
+                  kstep(std::false_type{}, std::true_type{});
+                  ++st;
+                  kstep(std::false_type{}, std::true_type{});
+                  ++st;
+              }
+          }
           if constexpr (!NO_T) {
               // T = 0 + S_0 (= S_0 exactly: an MFMA sum started from +0 is never -0),
               // then T + S_1, T + S_2, ... in fp32, round to nearest even
