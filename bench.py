@@ -417,7 +417,10 @@ def main():
         Xr, Wr = X[:, :ks].contiguous(), W[:ks].contiguous()
         # the per-rank kernel is the partials mode with one slice: S_p = X_p W_p, fp32
         T1 = T.view(1, w.M, w.N)
-        t_rank = _ev_time(torch, lambda: mmar.gemm_partials(Xr, Wr, 1, out=T1), reps)[0]
+        # back to back in batches of 10 launches (the kernel's own time; a single call
+        # after a synchronization also pays the launch latency, 8-10 us at this size)
+        t_rank = _ev_batch(torch, lambda: mmar.gemm_partials(Xr, Wr, 1, out=T1), reps)
+        t_rank_single = _ev_time(torch, lambda: mmar.gemm_partials(Xr, Wr, 1, out=T1), reps)[0]
         del Xr, Wr, T, T1
         torch.cuda.empty_cache()
         # the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16) and the
@@ -526,6 +529,9 @@ def main():
         result["per_rank_gemm"] = {"us": round(t_rank * 1e3, 2),
                                    "TFLOP/s": round(rank_flops / (t_rank * 1e-3) / 1e12, 2),
                                    "out_GBps": round(4.0 * w.M * w.N / (t_rank * 1e-3) / 1e9, 1),
+                                   "us_single_call": round(t_rank_single * 1e3, 2),
+                                   "timing": "median of batches of 10 launches back to back; "
+                                             "us_single_call: one launch after a synchronization",
                                    "shape": f"[{w.M},{w.K // P}] x [{w.K // P},{w.N}] -> fp32, one slice"}
         result["producer_gelu"] = {"us": round(t_prod * 1e3, 2),
                                    "TFLOP/s": round(flops / (t_prod * 1e-3) / 1e12, 2),
