@@ -158,39 +158,33 @@ __device__ __forceinline__ int swz_w(int k) {
 // sbase + voff0 - 1024 and lands at lds_addr1 - 1024 + 16 lane, copy 1 reads
 // sbase + voff1 and lands at lds_addr1 + 16 lane.  The instruction offset applies to both
 // addresses, so voff0 holds its byte offset plus 1024 (no wrap: an offset within a tile
-// of X, W or W^T, each under 2^31 elements, stays far below 2^32 - 1024).  M0 is saved and
-// restored.  Inline asm, so that the compiler does not turn
-// the LDS writes into a wait on every later LDS read; the kernel waits on the
-// vector-memory counter itself.  One M0 setting per pair instead of per copy saved about
-// an eighth of the instructions a wave issues per K step.
+// of X, W or W^T, each under 2^31 elements, stays far below 2^32 - 1024).  M0 is
+// declared clobbered (the compiler keeps nothing of its own in it across the asm).  Inline
+// asm, so that the compiler does not turn the LDS writes into a wait on every later LDS
+// read; the kernel waits on the vector-memory counter itself.  One M0 setting per pair
+// instead of per copy saved about an eighth of the instructions a wave issues per K step.
 __device__ __forceinline__ void dma16x2(const void* sbase, uint32_t voff0, uint32_t voff1,
                                         uint32_t lds_addr1) {
-    uint32_t saved;
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %4\n\t"
+        "s_mov_b32 m0, %3\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %3 offset:-1024\n\t"
-        "global_load_lds_dwordx4 %2, %3\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
+        "global_load_lds_dwordx4 %0, %2 offset:-1024\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
         : "v"(voff0), "v"(voff1), "s"(sbase), "s"(lds_addr1)
-        : "memory");
+        : "memory", "m0");
 }
 
 // One 16-byte global -> LDS copy per lane: reads sbase + voff, lands at lds_addr + 16 lane
-// (lds_addr wave-uniform).  M0 is saved and restored.
+// (lds_addr wave-uniform).  M0 is declared clobbered.
 __device__ __forceinline__ void dma16x1(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-    uint32_t saved;
     asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %3\n\t"
+        "s_mov_b32 m0, %2\n\t"
         "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
+        "global_load_lds_dwordx4 %0, %1"
+        :
         : "v"(voff), "s"(sbase), "s"(lds_addr)
-        : "memory");
+        : "memory", "m0");
 }
 
 // Byte bias a copy's per-lane source offset carries against its instruction offset: +1 KB
@@ -359,29 +353,29 @@ void tile_kernel(TileArgs a) {
         // residual copy pair j (j < XOPS) issued during K step cur, one of the last two
         // (cur = nsteps - 2 + half): residual rows 128 half .. +127 into the X stage of step
         // cur + LEAD, which the repeat of the last step's X operands would have filled
-        auto res_copy_op = [&](int j, int cur) {
+        // (xsi: that stage, (cur + LEAD) mod XSTAGES)
+        auto res_copy_op = [&](int j, int cur, unsigned xsi) {
             const int i = 2 * j, half = cur + C::LEAD - nsteps;
-            const uint32_t xd = lds_addr(xs_base + xstage(cur + C::LEAD) * C::XS +
-                                         (C::XQ * uwave + i + 1) * 512);
+            const uint32_t xd = lds_addr(xs_base + xsi * C::XS + (C::XQ * uwave + i + 1) * 512);
             dma16x2(uniform_ptr(a.residual + (static_cast<int64_t>(m0) + 128 * half) * a.ldr + n0),
                     roff[i], roff[i + 1], xd);
         };
-        // copy operation j of step st: X copies 2j, 2j+1 (j < XOPS), else W copies q, q+1
-        // (q = 2 (j - XOPS)), or W copy q alone when it is the last of an odd count
-        auto copy_op = [&](int st, int j) {
+        // copy operation j of step st into X stage xsi and W stage wsi: X copies 2j, 2j+1
+        // (j < XOPS), else W copies q, q+1 (q = 2 (j - XOPS)), or W copy q alone when it is
+        // the last of an odd count
+        auto copy_op = [&](int st, unsigned xsi, unsigned wsi, int j) {
             if (j < C::XOPS) {
                 const int i = 2 * j;
-                const uint32_t xd = lds_addr(xs_base + xstage(st) * C::XS +
-                                             (C::XQ * uwave + i + 1) * 512);
+                const uint32_t xd = lds_addr(xs_base + xsi * C::XS + (C::XQ * uwave + i + 1) * 512);
                 dma16x2(step_ptr(xbase, st, xstep_b), xoff[i], xoff[i + 1], xd);
             } else {
                 const int q = 2 * (j - C::XOPS);
                 if (q + 1 < C::WQ) {
-                    const uint32_t wd = lds_addr(ws_base + wstage(st) * C::WS +
+                    const uint32_t wd = lds_addr(ws_base + wsi * C::WS +
                                                  (C::WQ * uwave + q + 1) * 512);
                     dma16x2(step_ptr(wbase, st, wstep_b), woff[q], woff[q + 1], wd);
                 } else {
-                    const uint32_t wd = lds_addr(ws_base + wstage(st) * C::WS +
+                    const uint32_t wd = lds_addr(ws_base + wsi * C::WS +
                                                  (C::WQ * uwave + q) * 512);
                     dma16x1(step_ptr(wbase, st, wstep_b), woff[q], wd);
                 }
@@ -400,15 +394,15 @@ void tile_kernel(TileArgs a) {
             }
 
         const int last = nsteps - 1;
-        // operand fragment of row block mb (X) / column block nb (W) for MFMA k step s of
-        // K step t
-        auto read_x = [&](int t, int s, int mb) -> bf16x8 {
-            const uint16_t* xs = xs_base + xstage(t) * C::XS;
+        // operand fragment of row block mb (X) / column block nb (W) for MFMA k step s,
+        // from X stage xsi / W stage wsi
+        auto read_x = [&](unsigned xsi, int s, int mb) -> bf16x8 {
+            const uint16_t* xs = xs_base + xsi * C::XS;
             const int m = C::RW * wm + 32 * mb + l32;
             return *reinterpret_cast<const bf16x8*>(xs + xrd[mb] + 8 * ((2 * s + h) ^ swz_x<BK>(m)));
         };
-        auto read_w = [&](int t, int s, int nb) -> bf16x8 {
-            const uint16_t* wsb = ws_base + wstage(t) * C::WS;
+        auto read_w = [&](unsigned wsi, int s, int nb) -> bf16x8 {
+            const uint16_t* wsb = ws_base + wsi * C::WS;
             if constexpr (WT) {
                 const int n = C::CW * wn + 32 * nb + l32;
                 return *reinterpret_cast<const bf16x8*>(wsb + n * BK +
@@ -424,11 +418,11 @@ void tile_kernel(TileArgs a) {
                 return __builtin_bit_cast(bf16x8, both);
             }
         };
-        auto frags = [&](int t, int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
+        auto frags = [&](unsigned xsi, unsigned wsi, int s, bf16x8 (&xf)[MB], bf16x8 (&wf)[NB]) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb) xf[mb] = read_x(t, s, mb);
+            for (int mb = 0; mb < MB; ++mb) xf[mb] = read_x(xsi, s, mb);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) wf[nb] = read_w(t, s, nb);
+            for (int nb = 0; nb < NB; ++nb) wf[nb] = read_w(wsi, s, nb);
         };
         // Step-boundary handshake for K step t: this wave's copies of t are done (only the
         // copies of the LEAD - 1 following steps may remain) and the barrier makes every
@@ -444,7 +438,7 @@ void tile_kernel(TileArgs a) {
 #pragma unroll
         for (int d = 0; d < C::LEAD; ++d)
 #pragma unroll
-            for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), j);
+            for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), d, d, j);
         handshake();
 
         // running-total blocks (nb = NB - 1, mb < TLDS) kept in this wave's LDS area (the
@@ -494,8 +488,8 @@ void tile_kernel(TileArgs a) {
                     constexpr int i = decltype(ic)::value, mb = i / NB, nb = i % NB;
                     S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                         wf0[nb], xf0[mb], ZERO ? f32x16{} : S[nb][mb], 0, 0, 0);
-                    if constexpr (i < NB) wf1[i] = read_w(st, 1, i);
-                    else if constexpr (i < NB + MB) xf1[i - NB] = read_x(st, 1, i - NB);
+                    if constexpr (i < NB) wf1[i] = read_w(wstage(st), 1, i);
+                    else if constexpr (i < NB + MB) xf1[i - NB] = read_x(xstage(st), 1, i - NB);
                     if constexpr (i == 3) {
                         xsrc = step_ptr(xbase, st2, xstep_b);
                         xdst = lds_addr(xs_base + xstage(st2) * C::XS + C::XQ * uwave * 512);
@@ -519,8 +513,8 @@ void tile_kernel(TileArgs a) {
                     constexpr int i = decltype(ic)::value, mb = i / NB, nb = i % NB;
                     S[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf1[nb], xf1[mb],
                                                                         S[nb][mb], 0, 0, 0);
-                    if constexpr (i < NB) wf0[i] = read_w(nx, 0, i);
-                    else if constexpr (i < NB + MB) xf0[i - NB] = read_x(nx, 0, i - NB);
+                    if constexpr (i < NB) wf0[i] = read_w(wstage(nx), 0, i);
+                    else if constexpr (i < NB + MB) xf0[i - NB] = read_x(xstage(nx), 0, i - NB);
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
@@ -569,7 +563,13 @@ void tile_kernel(TileArgs a) {
         // fragments are double-buffered: k step s of any K step uses buffer s % 2 (KS is
         // even), and the first fragments of step t+1 are read during the last MFMAs of t
         bf16x8 xa[MB], wa[NB], xb2[MB], wb2[NB];
-        frags(0, 0, xa, wa);
+        frags(0, 0, 0, xa, wa);
+        // ring stages of step st, kept as running indices instead of st mod XSTAGES / mod
+        // WSTAGES recomputed per use
+        unsigned x3 = 0, w4 = 0;
+        auto ring_next = [](unsigned i, unsigned n, unsigned by) {
+            return i + by >= n ? i + by - n : i + by;
+        };
 
         // One K step (step st): KS k steps of NB x MB MFMAs, the copies of step st+LEAD between
         // them, the step-boundary handshake before the last k step.  ZERO marks the first
@@ -580,9 +580,13 @@ void tile_kernel(TileArgs a) {
             // RES: one of the last two K steps of a tile whose residual goes through LDS;
             // its X copy slots carry residual copies (the same number of copies per step)
             constexpr bool RES = decltype(res_tag)::value;
-            // copies of step st+LEAD (the last steps re-copy the last one: identical bytes,
-            // no branch), spread over the MFMAs of k steps 0 .. KS-2
+            // copies of step st+LEAD, spread over the MFMAs of k steps 0 .. KS-2.  The last
+            // LEAD steps of an item copy the last step's operands again (the same count of
+            // copies every step) into the stages of steps st + LEAD, which follow the
+            // item's last step: nothing reads them before the item's final drain.
             const int st2 = min(st + C::LEAD, last);
+            const unsigned xc = ring_next(x3, C::XSTAGES, C::LEAD);
+            const unsigned wc = ring_next(w4, C::WSTAGES, C::LEAD);
             // the NB x MB MFMAs of one k step, with copy operations c0 .. c1-1 issued between
             // them (all of them: the caller passes c1 - c0 <= OPS)
             auto mfmas = [&](const bf16x8 (&xf)[MB], const bf16x8 (&wf)[NB], int c0, int c1,
@@ -601,11 +605,11 @@ void tile_kernel(TileArgs a) {
                             __builtin_amdgcn_sched_barrier(0);
                             if constexpr (RES) {
                                 if (c < C::XOPS)
-                                    res_copy_op(c, st);
+                                    res_copy_op(c, st, xc);
                                 else
-                                    copy_op(st2, c);
+                                    copy_op(st2, xc, wc, c);
                             } else {
-                                copy_op(st2, c);
+                                copy_op(st2, xc, wc, c);
                             }
                             c += 1;
                             __builtin_amdgcn_sched_barrier(0);
@@ -616,16 +620,17 @@ void tile_kernel(TileArgs a) {
 #pragma unroll
             for (int s = 0; s < KS; s += 2) {
                 // k step s (buffer a), prefetching s+1 into buffer b
-                frags(st, s + 1, xb2, wb2);
+                frags(x3, w4, s + 1, xb2, wb2);
                 mfmas(xa, wa, min(s * CPS, C::OPS), min((s + 1) * CPS, C::OPS), ZERO && s == 0);
-                // k step s+1 (buffer b), prefetching s+2, or the next K step's first
+                // k step s+1 (buffer b), prefetching s+2, or the next K step's first (after
+                // an item's last step: fragments of a stage being refilled, never used)
                 if (s + 2 < KS) {
-                    frags(st, s + 2, xa, wa);
+                    frags(x3, w4, s + 2, xa, wa);
                     mfmas(xb2, wb2, min((s + 1) * CPS, C::OPS), min((s + 2) * CPS, C::OPS),
                           false);
                 } else {
                     handshake();
-                    frags(min(st + 1, last), 0, xa, wa);
+                    frags(ring_next(x3, C::XSTAGES, 1), ring_next(w4, C::WSTAGES, 1), 0, xa, wa);
                     mfmas(xb2, wb2, C::OPS, C::OPS, false);
                 }
             }
@@ -633,18 +638,26 @@ void tile_kernel(TileArgs a) {
 
         // the slices' K steps; with the residual through LDS the last two steps of the
         // last slice are the residual variant (peeled after one loop with a shorter bound)
+        auto advance = [&]() {
+            ++st;
+            x3 = ring_next(x3, C::XSTAGES, 1);
+            w4 = ring_next(w4, C::WSTAGES, 1);
+        };
         for (int p = p_lo; p < p_hi; ++p) {
           const bool peel = RES_OK && use_res && p == p_hi - 1;
           kstep(std::true_type{}, std::false_type{});
-          ++st;
+          advance();
           const int jend = peel ? sps - 2 : sps;
-          for (int j = 1; j < jend; ++j, ++st) kstep(std::false_type{}, std::false_type{});
+          for (int j = 1; j < jend; ++j) {
+              kstep(std::false_type{}, std::false_type{});
+              advance();
+          }
           if constexpr (RES_OK) {
               if (peel) {
                   kstep(std::false_type{}, std::true_type{});
-                  ++st;
+                  advance();
                   kstep(std::false_type{}, std::true_type{});
-                  ++st;
+                  advance();
               }
           }
           if constexpr (!NO_T) {
