@@ -783,14 +783,17 @@ void med_iqr(std::vector<float> t, float* med, float* iqr) {
     *iqr = t[(3 * n) / 4] - t[n / 4];
 }
 
-// Times every candidate plan `rounds` times, interleaved (round r runs every candidate once)
-// so that clock drift and thermal state affect all candidates alike.  Each round starts
-// with one untimed call (the first launch after the round's synchronization meets an idle
-// GPU) and runs the candidates in an order rotated by one per round, so no candidate is
-// always first or always after the same one.  times[i] gets candidate i's per-call
-// durations in ms.
+// Times every candidate plan `rounds` times, interleaved (round r runs every candidate
+// once) so that clock drift and thermal state affect all candidates alike.  A sample is
+// `batch` calls back to back between two events, divided by `batch`: calls queued behind
+// each other, as in a model's step, where a schedule of several kernels overlaps its
+// launches and a lone call after a synchronization would add the launch latency and the
+// idle GPU's clock recovery (the single-call spread was 2-5 % of the block).  Each round
+// starts with one untimed call and runs the candidates in an order rotated by one per
+// round, so no candidate is always first or always after the same one.  times[i] gets
+// candidate i's per-call durations in ms.
 int time_plans(DevState* st, const Call& c, const std::vector<Plan>& plans, int rounds,
-               hipStream_t s, std::vector<std::vector<float>>* times) {
+               int batch, hipStream_t s, std::vector<std::vector<float>>* times) {
     const size_t n = plans.size();
     times->assign(n, {});
     std::vector<hipEvent_t> ev(2 * n, nullptr);
@@ -804,7 +807,8 @@ int time_plans(DevState* st, const Call& c, const std::vector<Plan>& plans, int 
         for (size_t j = 0; j < n && !rc; ++j) {
             const size_t i = (j + static_cast<size_t>(r)) % n;
             if (hipEventRecord(ev[2 * i], s) != hipSuccess) rc = fail(MMAR_EHIP, "hipEventRecord");
-            if (!rc) rc = run_plan(st, c, plans[i], kRunFused, nullptr, 0, s);
+            for (int b = 0; b < batch && !rc; ++b)
+                rc = run_plan(st, c, plans[i], kRunFused, nullptr, 0, s);
             if (!rc && hipEventRecord(ev[2 * i + 1], s) != hipSuccess)
                 rc = fail(MMAR_EHIP, "hipEventRecord");
         }
@@ -813,7 +817,7 @@ int time_plans(DevState* st, const Call& c, const std::vector<Plan>& plans, int 
             float ms = 0;
             if (hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]) != hipSuccess)
                 rc = fail(MMAR_EHIP, "hipEventElapsedTime");
-            (*times)[i].push_back(ms);
+            (*times)[i].push_back(ms / static_cast<float>(batch));
         }
     }
     for (auto& e : ev)
@@ -1511,10 +1515,10 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
     // and the tie goes to the earliest in candidate order (larger chunks, W read
     // directly, the 256 x 128 tile first), so that near-equal plans do not trade places
     // from box to box.
-    constexpr int kTuneRounds = 25;
+    constexpr int kTuneRounds = 25, kTuneBatch = 4;
     constexpr float kMinGain = 0.01f;
     std::vector<std::vector<float>> times;
-    rc = time_plans(st, c, cands, kTuneRounds, stream, &times);
+    rc = time_plans(st, c, cands, kTuneRounds, kTuneBatch, stream, &times);
     cleanup();
     if (rc) return rc;
     std::vector<float> med(cands.size()), iqr(cands.size());

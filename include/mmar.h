@@ -318,8 +318,9 @@ int mmar_reduce_epilogue_only(const float* partials, const uint16_t* bias,
 
 /* The autotuner (CoCoNet picks its schedules by automatic search; "Key takeaways", first
  * bullet): times candidate {schedule, tile, chunk, weight mode} plans for this shape on
- * library-owned buffers, 25 rounds interleaved (each round runs every candidate once, in
- * an order rotated from round to round), and keeps the default plan unless a candidate's
+ * library-owned buffers, 25 rounds interleaved (each round times every candidate once, in
+ * an order rotated from round to round, as 4 calls back to back between two events), and
+ * keeps the default plan unless a candidate's
  * median time beats it by more than the larger of the two interquartile ranges and by at
  * least 1 % of the default's median; among such candidates the fastest wins, and a
  * candidate tied with it within their interquartile ranges wins instead if it comes
