@@ -44,6 +44,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -144,13 +145,21 @@ def _ev_time(torch, fn, reps, before=None, stats=False):
 TILE_KERNEL_SOURCES = ("tile_kernel.hip", "device_common.h", "mmar_internal.h")
 
 
+def _code_only(text):
+    """C++ source without its comments and blank lines (no string literal in these
+    sources holds a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.split("\n"))
+    return "\n".join(ln for ln in lines if ln)
+
+
 def tile_kernel_sha():
-    """sha256 over the sources that define the fused tile kernel (its counters are valid
-    only for this exact code)."""
+    """sha256 over the code of the sources that define the fused tile kernel, comments and
+    blank lines left out (its counters are valid only for this exact code)."""
     h = hashlib.sha256()
     for name in TILE_KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "chunked_matmul_reduce_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "chunked_matmul_reduce_amd", "csrc", name)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 

@@ -16,8 +16,9 @@
 // four registers, four consecutive columns: exactly one Philox group, one 8-byte bias /
 // residual load and one 16-byte fp32 store, with no cross-lane exchange.
 //   * Staging: global_load_lds_dwordx4 copies (HBM/L2 -> LDS, no register round trip),
-//     issued in pairs that share one M0 setting, into a ring of X stages [256][BK] and a ring of W stages [BK][128] (W^T [128][BK]
-//     when W is given transposed), LEAD K steps ahead; 16-byte chunks are XOR-swizzled
+//     issued in pairs that share one M0 setting, into a ring of X stages [256][BK] and a
+//     ring of W stages [BK][128] (W^T [128][BK] when W is given transposed), LEAD K steps
+//     ahead; 16-byte chunks are XOR-swizzled
 //     so the copies and the operand reads are bank-conflict free.  W [K, N] operands are
 //     read with the LDS transpose read ds_read_b64_tr_b16, everything else with 16-byte
 //     reads.
@@ -42,8 +43,11 @@
 //     workgroup ids are remapped so the 32 workgroups resident on one XCD (ids are
 //     dealt round-robin over the 8 XCDs) take 32 consecutive items and share their
 //     X rows and W columns in that XCD's L2.
-//   * Epilogue: every bias and residual load of the tile is issued before the first
-//     Philox block is computed, so the load latency is paid once per tile.
+//   * Epilogue: on a full fp32-output tile the residual comes in through the X ring
+//     during the tile's last two K steps (their X copies would only repeat the last
+//     step's operands) and is read from LDS; otherwise every bias and residual load of
+//     the tile is issued before the first Philox block is computed, so the load latency
+//     is paid once per tile.
 //
 // No fused multiply-add anywhere in the epilogue (built with -ffp-contract=off and
 // written with explicit round-to-nearest add / multiply).
