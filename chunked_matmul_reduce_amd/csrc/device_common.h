@@ -44,12 +44,17 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-__device__ __forceinline__ float epi1(float t, float b, float r, uint32_t word,
-                                      const DropParams& d) {
-    const float v = __fadd_rn(t, b);
+// One output from v = T + bias: scaled if kept, then the residual added (dropped: the
+// residual itself).
+__device__ __forceinline__ float epi1_v(float v, float r, uint32_t word, const DropParams& d) {
     const float y = __fmul_rn(v, d.scale);
     const bool keep = (d.drop_all == 0u) && (word >= d.thr);
     return keep ? __fadd_rn(r, y) : r;
+}
+
+__device__ __forceinline__ float epi1(float t, float b, float r, uint32_t word,
+                                      const DropParams& d) {
+    return epi1_v(__fadd_rn(t, b), r, word, d);
 }
 
 // Epilogue of four consecutive outputs starting at linear index e (e % 4 == 0; e = m N + n
@@ -65,6 +70,19 @@ __device__ __forceinline__ float4 epilogue4(float4 t, uint2 bias, uint2 res, int
     o.y = epi1(t.y, bf16_hi(bias.x), bf16_hi(res.x), w.y, d);
     o.z = epi1(t.z, bf16_lo(bias.y), bf16_lo(res.y), w.z, d);
     o.w = epi1(t.w, bf16_hi(bias.y), bf16_hi(res.y), w.w, d);
+    return o;
+}
+
+// The same with the bias already added: v = T + bias.
+__device__ __forceinline__ float4 epilogue4_v(float4 v, uint2 res, int64_t e, const DropParams& d) {
+    const uint64_t g = static_cast<uint64_t>(e) >> 2;
+    const uint4 w = philox4x32_10(static_cast<uint32_t>(g), static_cast<uint32_t>(g >> 32),
+                                  d.ctr2, d.ctr3, d.key0, d.key1);
+    float4 o;
+    o.x = epi1_v(v.x, bf16_lo(res.x), w.x, d);
+    o.y = epi1_v(v.y, bf16_hi(res.x), w.y, d);
+    o.z = epi1_v(v.z, bf16_lo(res.y), w.z, d);
+    o.w = epi1_v(v.w, bf16_hi(res.y), w.w, d);
     return o;
 }
 

@@ -45,9 +45,11 @@
 //     X rows and W columns in that XCD's L2.
 //   * Epilogue: on a full fp32-output tile the residual comes in through the X ring
 //     during the tile's last two K steps (their X copies would only repeat the last
-//     step's operands) and is read from LDS; otherwise every bias and residual load of
-//     the tile is issued before the first Philox block is computed, so the load latency
-//     is paid once per tile.
+//     step's operands); the epilogue adds the bias, reads the residual from LDS into
+//     registers and, once every wave has, issues the next tile's first two K steps of
+//     copies, which land under its Philox arithmetic and stores.  Otherwise every bias
+//     and residual load of the tile is issued before the first Philox block is computed,
+//     so the load latency is paid once per tile.
 //
 // No fused multiply-add anywhere in the epilogue (built with -ffp-contract=off and
 // written with explicit round-to-nearest add / multiply).
@@ -266,7 +268,9 @@ void tile_kernel(TileArgs a) {
     const int wk = 8 * (grp >> 1) + (gi >> 2);            // row within a 16-row k step
     const int wcn = C::CW * wn + 16 * (grp & 1) + 4 * (gi & 3);   // column (block 0)
 
-    for (int item = slot; item < a.total_items; item += G) {
+    // Work item -> tile origin and extent (and slice range in the partials mode)
+    struct ItemTile { int m0, n0, rows, cols, p_lo, p_hi; };
+    auto tile_of = [&](int item) {
         int tile_item = item, p_lo = 0, p_hi = a.P;
         if (MODE == kModePartials) {
             tile_item = item % n_tiles;
@@ -280,14 +284,13 @@ void tile_kernel(TileArgs a) {
         const int gm = min(GM, tpcm - first_tm);
         const int tin = t - (t / (GM * tpcn)) * (GM * tpcn);
         const int tm = first_tm + tin % gm, tn = tin / gm;
-        const int m0 = a.rm0 + cr * a.cm + tm * BM;
-        const int n0 = a.rn0 + cc * a.cn + tn * BN;
-        const int rows = min(BM, a.cm - tm * BM), cols = min(BN, a.cn - tn * BN);
-
-        // Copy sources: a wave-uniform base (SGPRs) per K step plus per-lane byte
-        // offsets.  Copy q of wave w fills 16-byte chunks 64 (Q w + q) + lane of the
-        // stage; X rows are clamped to the tile, W columns to the tile.
-        uint32_t xoff[C::XQ], woff[C::WQ];
+        return ItemTile{a.rm0 + cr * a.cm + tm * BM, a.rn0 + cc * a.cn + tn * BN,
+                        min(BM, a.cm - tm * BM), min(BN, a.cn - tn * BN), p_lo, p_hi};
+    };
+    // Copy sources: a wave-uniform base (SGPRs) per K step plus per-lane byte offsets.
+    // Copy q of wave w fills 16-byte chunks 64 (Q w + q) + lane of the stage; X rows are
+    // clamped to the tile, W columns to the tile.
+    auto copy_offsets = [&](int rows, int cols, uint32_t (&xoff)[C::XQ], uint32_t (&woff)[C::WQ]) {
 #pragma unroll
         for (int q = 0; q < C::XQ; ++q) {
             const int idx = 64 * (C::XQ * wave + q) + lane;
@@ -313,8 +316,58 @@ void tile_kernel(TileArgs a) {
                     copy_bias<TILE, C::WQ>(q));
             }
         }
+    };
+    auto x_base = [&](const ItemTile& it) {
+        return static_cast<const uint16_t*>(
+            uniform_ptr(a.X + static_cast<int64_t>(it.m0) * a.ldx + static_cast<int64_t>(it.p_lo) * a.Ks));
+    };
+    auto w_base = [&](const ItemTile& it) {
+        const int64_t kf = static_cast<int64_t>(it.p_lo) * a.Ks;
+        return static_cast<const uint16_t*>(uniform_ptr(
+            WT ? a.W + static_cast<int64_t>(it.n0) * a.ldw + kf : a.W + kf * a.ldw + it.n0));
+    };
+    // bytes per K step; a step's byte offset st * step fits 32 bits (the extents of X
+    // and W, rows times leading dimension, are below 2^31 elements)
+    const uint32_t xstep_b = BK * 2;
+    const uint32_t wstep_b = WT ? BK * 2 : static_cast<uint32_t>(BK * a.ldw * 2);
+    auto step_ptr = [](const uint16_t* base, int st, uint32_t step_b) {
+        return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) +
+                                                 static_cast<uint32_t>(st) * step_b);
+    };
+    // copy operation j of step st from the bases and offsets of one item, into X stage xsi
+    // and W stage wsi: X copies 2j, 2j+1 (j < XOPS), else W copies q, q+1
+    // (q = 2 (j - XOPS)), or W copy q alone when it is the last of an odd count
+    auto copy_op_of = [&](const uint16_t* xb, const uint16_t* wb, const uint32_t (&xo)[C::XQ],
+                          const uint32_t (&wo)[C::WQ], int st, unsigned xsi, unsigned wsi, int j) {
+        if (j < C::XOPS) {
+            const int i = 2 * j;
+            const uint32_t xd = lds_addr(xs_base + xsi * C::XS + (C::XQ * uwave + i + 1) * 512);
+            dma16x2(step_ptr(xb, st, xstep_b), xo[i], xo[i + 1], xd);
+        } else {
+            const int q = 2 * (j - C::XOPS);
+            if (q + 1 < C::WQ) {
+                const uint32_t wd = lds_addr(ws_base + wsi * C::WS + (C::WQ * uwave + q + 1) * 512);
+                dma16x2(step_ptr(wb, st, wstep_b), wo[q], wo[q + 1], wd);
+            } else {
+                const uint32_t wd = lds_addr(ws_base + wsi * C::WS + (C::WQ * uwave + q) * 512);
+                dma16x1(step_ptr(wb, st, wstep_b), wo[q], wd);
+            }
+        }
+    };
+    // The next item's first LEAD K steps of copies may have been issued at the end of
+    // this one (a fused tile whose residual came through LDS: after its last LDS reads,
+    // before its Philox arithmetic and its 16 output stores per lane), so that they land
+    // under that epilogue; its first handshake then lets those stores stay in flight.
+    constexpr int kTileStores = 4 * NB * MB;   // 16-byte stores per lane of a full tile
+    bool prefetched = false;
+
+    for (int item = slot; item < a.total_items; item += G) {
+        const ItemTile itile = tile_of(item);
+        const int m0 = itile.m0, n0 = itile.n0, rows = itile.rows, cols = itile.cols;
+        const int p_lo = itile.p_lo, p_hi = itile.p_hi;
+        uint32_t xoff[C::XQ], woff[C::WQ];
+        copy_offsets(rows, cols, xoff, woff);
         const int nsteps = (p_hi - p_lo) * sps;
-        const int64_t k_first = static_cast<int64_t>(p_lo) * a.Ks;
 
         // The fused epilogue's residual tile through the X ring.  On a full tile whose
         // residual rows are 16-byte aligned, the last two K steps (whose copies would only
@@ -338,21 +391,11 @@ void tile_kernel(TileArgs a) {
                           copy_bias<TILE, C::XQ>(q);
             }
         }
-        const uint16_t* xbase = static_cast<const uint16_t*>(
-            uniform_ptr(a.X + static_cast<int64_t>(m0) * a.ldx + k_first));
-        const uint16_t* wbase = static_cast<const uint16_t*>(uniform_ptr(
-            WT ? a.W + static_cast<int64_t>(n0) * a.ldw + k_first : a.W + k_first * a.ldw + n0));
-        // bytes per K step; a step's byte offset st * step fits 32 bits (the extents of X
-        // and W, rows times leading dimension, are below 2^31 elements)
-        const uint32_t xstep_b = BK * 2;
-        const uint32_t wstep_b = WT ? BK * 2 : static_cast<uint32_t>(BK * a.ldw * 2);
+        const uint16_t* xbase = x_base(itile);
+        const uint16_t* wbase = w_base(itile);
         // stage of K step st (st >= 0: unsigned arithmetic keeps the modulo short)
         auto xstage = [](int st) { return static_cast<unsigned>(st) % C::XSTAGES; };
         auto wstage = [](int st) { return static_cast<unsigned>(st) % C::WSTAGES; };
-        auto step_ptr = [](const uint16_t* base, int st, uint32_t step_b) {
-            return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(base) +
-                                                     static_cast<uint32_t>(st) * step_b);
-        };
 
         // residual copy pair j (j < XOPS) issued during K step cur, one of the last two
         // (cur = nsteps - 2 + half): residual rows 128 half .. +127 into the X stage of step
@@ -364,26 +407,9 @@ void tile_kernel(TileArgs a) {
             dma16x2(uniform_ptr(a.residual + (static_cast<int64_t>(m0) + 128 * half) * a.ldr + n0),
                     roff[i], roff[i + 1], xd);
         };
-        // copy operation j of step st into X stage xsi and W stage wsi: X copies 2j, 2j+1
-        // (j < XOPS), else W copies q, q+1 (q = 2 (j - XOPS)), or W copy q alone when it is
-        // the last of an odd count
+        // copy operation j of step st of this item into X stage xsi and W stage wsi
         auto copy_op = [&](int st, unsigned xsi, unsigned wsi, int j) {
-            if (j < C::XOPS) {
-                const int i = 2 * j;
-                const uint32_t xd = lds_addr(xs_base + xsi * C::XS + (C::XQ * uwave + i + 1) * 512);
-                dma16x2(step_ptr(xbase, st, xstep_b), xoff[i], xoff[i + 1], xd);
-            } else {
-                const int q = 2 * (j - C::XOPS);
-                if (q + 1 < C::WQ) {
-                    const uint32_t wd = lds_addr(ws_base + wsi * C::WS +
-                                                 (C::WQ * uwave + q + 1) * 512);
-                    dma16x2(step_ptr(wbase, st, wstep_b), woff[q], woff[q + 1], wd);
-                } else {
-                    const uint32_t wd = lds_addr(ws_base + wsi * C::WS +
-                                                 (C::WQ * uwave + q) * 512);
-                    dma16x1(step_ptr(wbase, st, wstep_b), woff[q], wd);
-                }
-            }
+            copy_op_of(xbase, wbase, xoff, woff, st, xsi, wsi, j);
         };
 
         // S: this slice's sums; T: the running total (the 256 x 192 tile defines T at the
@@ -439,11 +465,36 @@ void tile_kernel(TileArgs a) {
             wg_barrier();
         };
 
+        if (!prefetched) {
 #pragma unroll
-        for (int d = 0; d < C::LEAD; ++d)
+            for (int d = 0; d < C::LEAD; ++d)
 #pragma unroll
-            for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), d, d, j);
-        handshake();
+                for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), d, d, j);
+            handshake();
+        } else {
+            // the copies of step 0 are done once all but the LEAD - 1 later steps' copies
+            // and the previous tile's stores are
+            MMAR_WAIT_VM_LDS((C::LEAD - 1) * C::DMA + kTileStores);
+            wg_barrier();
+        }
+        prefetched = false;
+        // the next item's first LEAD K steps of copies, issued while this item's epilogue
+        // still has its output stores to issue (stages 0 .. LEAD - 1 of both rings)
+        auto prefetch_next = [&]() {
+            const int nxt = item + G;
+            if (nxt >= a.total_items) return;
+            const ItemTile nt = tile_of(nxt);
+            uint32_t nxo[C::XQ], nwo[C::WQ];
+            copy_offsets(nt.rows, nt.cols, nxo, nwo);
+            const uint16_t* nxb = x_base(nt);
+            const uint16_t* nwb = w_base(nt);
+            const int nlast = (nt.p_hi - nt.p_lo) * sps - 1;
+#pragma unroll
+            for (int d = 0; d < C::LEAD; ++d)
+#pragma unroll
+                for (int j = 0; j < C::OPS; ++j) copy_op_of(nxb, nwb, nxo, nwo, min(d, nlast), d, d, j);
+            prefetched = true;
+        };
 
         // running-total blocks (nb = NB - 1, mb < TLDS) kept in this wave's LDS area (the
         // 256 x 192 tile): value 4q + j of lane l at float offset 256 (4 blk + q) + 4 l + j
@@ -830,10 +881,45 @@ void tile_kernel(TileArgs a) {
                     return *reinterpret_cast<const uint2*>(xs_base + xstage(last + 1 + (r >> 7)) * C::XS +
                                                            slot * 8 + (nl & 7));
                 };
-                store_all(store_f32, res_lds);
-                // every wave has read its residual from the ring before the next item's
-                // copies refill it
+                // v = T + bias, the epilogue's first add, before anything else: the bias
+                // loads are consumed (and waited for) before the next item's copies go out
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            f32x16& acc = T[nb][mb];
+                            acc[4 * g] = __fadd_rn(acc[4 * g], bf16_lo(bb[nb][g].x));
+                            acc[4 * g + 1] = __fadd_rn(acc[4 * g + 1], bf16_hi(bb[nb][g].x));
+                            acc[4 * g + 2] = __fadd_rn(acc[4 * g + 2], bf16_lo(bb[nb][g].y));
+                            acc[4 * g + 3] = __fadd_rn(acc[4 * g + 3], bf16_hi(bb[nb][g].y));
+                        }
+                // the whole residual into registers; once every wave has it, the ring may
+                // take the next item's first copies, which then run under this epilogue's
+                // Philox arithmetic and stores
+                uint2 rq[NB][4][MB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) rq[nb][g][mb] = res_lds(nb, g, mb);
                 wg_barrier();
+                if constexpr (C::NW == 8 && BK == 64) prefetch_next();
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int mb = 0; mb < MB; ++mb) {
+                            const int64_t m = m0 + C::RW * wm + 32 * mb + l32;
+                            const int64_t n = n0 + C::CW * wn + 32 * nb + 8 * g + 4 * h;
+                            const f32x16& acc = T[nb][mb];
+                            const float4 v = make_float4(acc[4 * g], acc[4 * g + 1],
+                                                         acc[4 * g + 2], acc[4 * g + 3]);
+                            store_f32(m * a.ldo + n, epilogue4_v(v, rq[nb][g][mb], m * a.N + n, a.drop));
+                        }
             } else {
                 // every residual load issued first, so they are in flight together (and
                 // under the Philox arithmetic) instead of one load latency per group
