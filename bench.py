@@ -23,7 +23,9 @@ the producer MatMul in front of the block (H = GeLU(X0 . W1 + b1), bf16; the sam
 count), the whole MLP (producer then block), the QKV projection in front of the GPT-2
 attention block (bias, no activation), and the data-parallel side (gradient
 average of P = 8 replicas + Adam step over BERT-large's 335M parameters, HBM-bound),
-beside PyTorch's mean + fused AdamW.
+beside PyTorch's mean + fused AdamW.  Then the other three block workloads, each with its
+own tuned plan (fused time, roofline fraction, the epilogue's exposed cost and hipBLASLt's
+plain GEMM of the same shape; --no-other-workloads skips them).
 
 The default warm-up (50 steps, about 30 ms) takes the GPU past the clock transient of
 its first launches; the timed steps then run at the sustained clock.
@@ -202,6 +204,72 @@ def _cpu_baseline(inp, w, budget_s):
                       f"{t_total:.1f} s"}
 
 
+def _other_workloads(torch, np, mmar, names, steps, warmup):
+    """The other block workloads, each with its own tuned plan: the fused call's mean launch
+    duration from two HIP events around ``steps`` back-to-back launches (as for the
+    headline), the epilogue's exposed cost from 100 alternating fused / GEMM-alone launches
+    against the epilogue alone, and hipBLASLt's plain GEMM of the same shape."""
+    from workload import WORKLOADS, make_inputs
+    out_all = {}
+    for name in names:
+        w = WORKLOADS[name]
+        inp = make_inputs(w)
+        d = {k: torch.from_numpy(inp[k].view(np.int16)).to("cuda").view(torch.bfloat16)
+             for k in ("X", "W", "bias", "residual")}
+        del inp
+        X, W, bias, res = d["X"], d["W"], d["bias"], d["residual"]
+        P, p, seed = w.P, w.p_drop, w.seed
+        out = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        T = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+
+        def fused():
+            mmar.fused(X, W, bias, res, P, p, seed, out=out)
+        for _ in range(warmup):
+            fused()
+        torch.cuda.synchronize()
+        mmar.autotune(w.M, w.N, w.K, P)
+        plan = mmar.get_plan(w.M, w.N, w.K, P)
+        for _ in range(10):
+            fused()
+        s = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for _ in range(steps):
+            fused()
+        e1.record(s)
+        torch.cuda.synchronize()
+        t_f = e0.elapsed_time(e1) / steps
+        pers = lambda: mmar.fused_ex(X, W, bias, res, P, p, seed, "persistent", chunk=plan["chunk"]
+                                     if plan["schedule"] == 3 else (0, 0), w_mode="direct",
+                                     tile=plan["tile"], out=out)
+        _, _, pr_d, pr_iqr = _paired(torch, pers, lambda: mmar.gemm_only(X, W, P, out=T), 100)
+        mmar.gemm_only(X, W, P, out=T)
+        t_epi = _ev_time(torch, lambda: mmar.reduce_epilogue_only(T[None], bias, res, p, seed,
+                                                                  out=out), 20)[0]
+        Cv = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
+        t_v, t_fb = _ev_batches_ab(torch, lambda: torch.matmul(X, W, out=Cv), fused, 10, warm=100)
+        ach = w.flops / (t_f * 1e-3) / 1e12
+        out_all[name] = {
+            "shape": {"M": w.M, "K": w.K, "N": w.N, "P": P},
+            "plan": {"schedule": {1: "sequential", 2: "streams", 3: "persistent",
+                                  4: "balanced"}[plan["schedule"]],
+                     "chunk": list(plan["chunk"]),
+                     "w_mode": {0: "direct", 1: "pretranspose"}[plan["w_mode"]],
+                     "tile": {0: "256x128", 1: "256x192"}[plan["tile"]]},
+            "fused_us": round(t_f * 1e3, 2), "TFLOP/s": round(ach, 2),
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+            "paired_fused_minus_gemm_us": round(pr_d * 1e3, 2), "paired_iqr_us": round(pr_iqr * 1e3, 2),
+            "epi_alone_us": round(t_epi * 1e3, 2),
+            "hidden_fraction_epilogue": round(min(1.0, max(0.0, 1.0 - pr_d / t_epi)), 4),
+            "vendor_gemm_bf16_us": round(t_v * 1e3, 2),
+            "fused_over_vendor_time": round(t_fb / t_v, 3)}
+        del d, X, W, bias, res, out, T, Cv
+        torch.cuda.empty_cache()
+    return out_all
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +281,8 @@ def main():
                     default="all")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the summary of the other block workloads")
     ap.add_argument("--no-autotune", action="store_true",
                     help="time the default plan instead of the autotuned one")
     ap.add_argument("--tile", choices=["auto", "256x128", "256x192"], default="auto",
@@ -565,6 +635,11 @@ def main():
         result["re_alone_GBps"] = round(re_bytes / (t_re * 1e-3) / 1e9, 1)
         result["epi_alone_GBps"] = round(epi_bytes / (t_epi * 1e-3) / 1e9, 1)
 
+    if args.only == "all" and not args.no_other_workloads:
+        del X, W, bias, res, out, d
+        torch.cuda.empty_cache()
+        others = [n for n in ("gpt2_attn", "gpt2_mlp", "bert_mlp", "gpt3_mlp") if n != w.name]
+        result["other_workloads"] = _other_workloads(torch, np, mmar, others, 20, 20)
     if not args.no_cpu_baseline and args.only == "all":
         result["cpu_baseline"] = _cpu_baseline(inp, w, args.cpu_budget)
     print(json.dumps(result), flush=True)

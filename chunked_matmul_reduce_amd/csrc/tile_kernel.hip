@@ -471,6 +471,14 @@ void tile_kernel(TileArgs a) {
 #pragma unroll
                 for (int j = 0; j < C::OPS; ++j) copy_op(min(d, last), d, d, j);
             handshake();
+            // the 256 x 192 tile issues each step's X copies in the k step before its W
+            // copies (right after the handshake that frees their stage), so step LEAD's X
+            // copies go out here and its W copies in the first K step
+            if constexpr (TILE == kTile192) {
+#pragma unroll
+                for (int j = 0; j < C::XOPS; ++j)
+                    copy_op(min(C::LEAD, last), xstage(min(C::LEAD, last)), 0, j);
+            }
         } else {
             // the copies of step 0 are done once all but the LEAD - 1 later steps' copies
             // and the previous tile's stores are
@@ -509,8 +517,9 @@ void tile_kernel(TileArgs a) {
             // MFMAs go row block by row block (mb outer); an X fragment is re-read for the
             // next k step as soon as the three MFMAs of its row block are issued, the W
             // fragments of the next k step are read into the other half of a double buffer
-            // at the start of a k step.  All copies of step st + LEAD go between the MFMAs
-            // of the first k step, the handshake before the second.
+            // at the start of a k step.  The W copies of step st + LEAD go between the MFMAs
+            // of the first k step, the handshake before the second, and the X copies of
+            // step st + LEAD + 1 between the MFMAs of the second.
             static_assert(KS == 2, "the 256 x 192 tile steps K by 32");
             static_assert(C::XQ == 4 && C::WQ == 3, "copy groups of the 256 x 192 tile");
             // Fragments double-buffered: buffer 0 holds k step 0 of a K step, buffer 1 k
@@ -525,17 +534,24 @@ void tile_kernel(TileArgs a) {
             // One K step as two k steps of 12 MFMA slots each (mb outer, nb inner).  A single
             // wave per SIMD issues in order, so each slot holds one MFMA and at most a few
             // other instructions, which then issue while the MFMA runs: in k step 0 the
-            // fragment reads for k step 1 (W first, then X in MFMA order), then the X and W
-            // copies of step st + LEAD, then the handshake in the last slot (by then the
-            // reads it waits for have long returned); in k step 1 the reads of the next K
-            // step's first fragments.
+            // fragment reads for k step 1 (W first, then X in MFMA order), the W copies of
+            // step st + LEAD and the handshake in the last slot (by then the reads it waits
+            // for have long returned); in k step 1 the reads of the next K step's first
+            // fragments and the X copies of step st + LEAD + 1.  So the copies that fill a
+            // stage go out between the handshake that frees it and the next one, in four
+            // groups five slots apart: bunched into four consecutive slots, the four waves'
+            // copies of a step made the GPT-2 MLP block 3-4 % slower.  The handshake of step
+            // st still finds exactly the copies of the two newest such windows in flight.
             auto kstep192 = [&](auto zero_tag) {
                 constexpr bool ZERO = decltype(zero_tag)::value;
                 const int st2 = min(st + C::LEAD, last);
+                const int st3 = min(st + C::LEAD + 1, last);
                 const int nx = min(st + 1, last);
-                // copy sources and LDS destinations of step st2, computed in slots 3 and 4,
-                // used by the four copy operations in slots 7-10 (X pair, X pair, W pair,
-                // W single)
+                constexpr int K0A = 2, K0B = 7, K1A = 2, K1B = 7;
+                // copy sources and LDS destinations: W of step st2 (computed in slot K0A - 1,
+                // a pair in slot K0A and a single copy in K0B of k step 0), X of step st3
+                // (slot K1A - 1, pairs in slots K1A and K1B of k step 1); past an item's last
+                // step they repeat its operands
                 const uint16_t* xsrc = nullptr;
                 const uint16_t* wsrc = nullptr;
                 uint32_t xdst = 0, wdst = 0;
@@ -545,19 +561,12 @@ void tile_kernel(TileArgs a) {
                         wf0[nb], xf0[mb], ZERO ? f32x16{} : S[nb][mb], 0, 0, 0);
                     if constexpr (i < NB) wf1[i] = read_w(wstage(st), 1, i);
                     else if constexpr (i < NB + MB) xf1[i - NB] = read_x(xstage(st), 1, i - NB);
-                    if constexpr (i == 3) {
-                        xsrc = step_ptr(xbase, st2, xstep_b);
-                        xdst = lds_addr(xs_base + xstage(st2) * C::XS + C::XQ * uwave * 512);
-                    } else if constexpr (i == 4) {
+                    if constexpr (i == K0A - 1) {
                         wsrc = step_ptr(wbase, st2, wstep_b);
                         wdst = lds_addr(ws_base + wstage(st2) * C::WS + C::WQ * uwave * 512);
-                    } else if constexpr (i == 7) {
-                        dma16x2(xsrc, xoff[0], xoff[1], xdst + 1024);
-                    } else if constexpr (i == 8) {
-                        dma16x2(xsrc, xoff[2], xoff[3], xdst + 3072);
-                    } else if constexpr (i == 9) {
+                    } else if constexpr (i == K0A) {
                         dma16x2(wsrc, woff[0], woff[1], wdst + 1024);
-                    } else if constexpr (i == 10) {
+                    } else if constexpr (i == K0B) {
                         dma16x1(wsrc, woff[2], wdst + 2048);
                     } else if constexpr (i == MB * NB - 1) {
                         handshake();
@@ -570,6 +579,14 @@ void tile_kernel(TileArgs a) {
                                                                         S[nb][mb], 0, 0, 0);
                     if constexpr (i < NB) wf0[i] = read_w(wstage(nx), 0, i);
                     else if constexpr (i < NB + MB) xf0[i - NB] = read_x(xstage(nx), 0, i - NB);
+                    if constexpr (i == K1A - 1) {
+                        xsrc = step_ptr(xbase, st3, xstep_b);
+                        xdst = lds_addr(xs_base + xstage(st3) * C::XS + C::XQ * uwave * 512);
+                    } else if constexpr (i == K1A) {
+                        dma16x2(xsrc, xoff[0], xoff[1], xdst + 1024);
+                    } else if constexpr (i == K1B) {
+                        dma16x2(xsrc, xoff[2], xoff[3], xdst + 3072);
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
