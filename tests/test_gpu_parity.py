@@ -130,6 +130,40 @@ def test_ragged_shapes_against_oracle(M, K, N, P):
     assert np.array_equal(f32_bits(host(out)), ref)
 
 
+# ---------------------------------------------------------------- seeded shape sweep
+def _sweep_shapes(n, seed=20261203):
+    """n seeded random shapes inside the library's preconditions: M, N multiples of 32,
+    K/P a multiple of 32 (odd multiples take the 32-deep K step, few steps per item
+    exercise the copy clamping at an item's end), ragged against both tile shapes."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = 32 * int(rng.integers(1, 40))
+        N = 32 * int(rng.integers(1, 24))
+        P = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+        ks = 32 * int(rng.integers(1, 9))
+        out.append((M, ks * P, N, P))
+    return out
+
+
+@pytest.mark.parametrize("M,K,N,P", _sweep_shapes(10))
+def test_seeded_shape_sweep(M, K, N, P):
+    inp = make_random_inputs(M, K, N, seed=7 * M + 5 * K + 3 * N + P)
+    inp.update(M=M, K=K, N=N, P=P, p_drop=np.float32(0.15), seed=(N << 32) + M + P)
+    d = _to_dev(inp)
+    print("sweep", M, K, N, P, flush=True)
+    ref = None
+    for sched, tile in PLANS:
+        chunk = (0, 0)
+        if sched in ("sequential", "streams") and M % 64 == 0:
+            chunk = (M // 2, N)
+        out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk, tile=tile)
+        if ref is None:
+            _check_block(inp, out)
+            ref = f32_bits(out)
+        assert np.array_equal(f32_bits(out), ref), (sched, tile, chunk)
+
+
 # ---------------------------------------------------------------- full-size workloads
 @pytest.mark.parametrize("name", ["gpt2_attn", "gpt2_mlp", "bert_mlp", "gpt3_mlp"])
 def test_full_size_workload(name):
