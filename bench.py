@@ -254,7 +254,7 @@ def _other_workloads(torch, np, mmar, names, steps, warmup):
         out_all[name] = {
             "shape": {"M": w.M, "K": w.K, "N": w.N, "P": P},
             "plan": {"schedule": {1: "sequential", 2: "streams", 3: "persistent",
-                                  4: "balanced"}[plan["schedule"]],
+                                  4: "balanced", 5: "split"}[plan["schedule"]],
                      "chunk": list(plan["chunk"]),
                      "w_mode": {0: "direct", 1: "pretranspose"}[plan["w_mode"]],
                      "tile": {0: "256x128", 1: "256x192"}[plan["tile"]]},
@@ -417,7 +417,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.desc}", "M": w.M, "K": w.K, "N": w.N, "P": P,
                    "p_drop": p, "seed": seed, "out_dtype": "fp32", "accumulate": "fp32",
                    "plan": {"schedule": {1: "sequential", 2: "streams", 3: "persistent",
-                                         4: "balanced"}[plan["schedule"]],
+                                         4: "balanced", 5: "split"}[plan["schedule"]],
                             "chunk": list(plan["chunk"]), "ring": plan["ring"],
                             "w_mode": {0: "direct", 1: "pretranspose"}[plan["w_mode"]],
                             "tile": {0: "256x128", 1: "256x192"}[plan["tile"]]}},

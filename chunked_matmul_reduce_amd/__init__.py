@@ -26,8 +26,9 @@ LIB_PATH = os.path.join(_HERE, "libmmar.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mmar.h")
 
 OK, EINVAL, EALIGN, ENODEV, ENOMEM, EHIP = 0, -1, -2, -3, -4, -5
-SCHED_AUTO, SCHED_SEQUENTIAL, SCHED_STREAMS, SCHED_PERSISTENT, SCHED_BALANCED = 0, 1, 2, 3, 4
-SCHEDULES = {"auto": 0, "sequential": 1, "streams": 2, "persistent": 3, "balanced": 4}
+SCHED_AUTO, SCHED_SEQUENTIAL, SCHED_STREAMS, SCHED_PERSISTENT, SCHED_BALANCED, SCHED_SPLIT = (
+    0, 1, 2, 3, 4, 5)
+SCHEDULES = {"auto": 0, "sequential": 1, "streams": 2, "persistent": 3, "balanced": 4, "split": 5}
 W_AUTO, W_DIRECT, W_PRETRANSPOSE = -1, 0, 1
 W_MODES = {"auto": -1, "direct": 0, "pretranspose": 1}
 TILE_AUTO, TILE_256x128, TILE_256x192 = -1, 0, 1

@@ -50,7 +50,8 @@ struct Plan {
     int wmode = MMAR_W_AUTO;   // MMAR_W_DIRECT or MMAR_W_PRETRANSPOSE once resolved
     int tile = MMAR_TILE_AUTO; // MMAR_TILE_256x128 or MMAR_TILE_256x192 once resolved: the
                                // fused tile kernel's shape (persistent and balanced schedules)
-    int hm = 0, hn = 0;        // MMAR_SCHED_BALANCED: head block [0, hm) x [0, hn) (0: none)
+    int hm = 0, hn = 0;        // MMAR_SCHED_BALANCED / _SPLIT: head block [0, hm) x [0, hn)
+                               // (0: none)
     float margin_ms = 0.0f;    // autotuned plans: by how much (ms) the plan beat the default
                                // beyond the run-to-run spread (0: the default was kept)
 };
@@ -113,7 +114,7 @@ int check_chunk(const Shape& s, int32_t cm, int32_t cn) {
 }
 
 int check_sched(int32_t sched, int32_t ring, int32_t wmode, int32_t tile) {
-    if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_BALANCED)
+    if (sched < MMAR_SCHED_AUTO || sched > MMAR_SCHED_SPLIT)
         return fail(MMAR_EINVAL, "unknown schedule");
     if (ring < 0 || ring > kMaxRing) return fail(MMAR_EINVAL, "ring must be in [0, 8]");
     if (wmode < MMAR_W_AUTO || wmode > MMAR_W_PRETRANSPOSE)
@@ -289,7 +290,7 @@ Plan resolve(const Shape& s, Plan p, int cus) {
     if (p.sched == MMAR_SCHED_AUTO) p.sched = MMAR_SCHED_PERSISTENT;
     if (p.tile == MMAR_TILE_AUTO) p.tile = default_tile(s);
     if (p.sched == MMAR_SCHED_SEQUENTIAL || p.sched == MMAR_SCHED_STREAMS) p.tile = MMAR_TILE_256x128;
-    if (p.sched == MMAR_SCHED_BALANCED) {
+    if (p.sched == MMAR_SCHED_BALANCED || p.sched == MMAR_SCHED_SPLIT) {
         p.cm = static_cast<int>(s.M);
         p.cn = static_cast<int>(s.N);
         p.ring = 0;
@@ -358,7 +359,8 @@ bool plan_is_valid(const Shape& s, const Plan& p) {
                           s.M % p.cm == 0 && s.N % p.cn == 0;
     const bool sched_ok = p.sched == MMAR_SCHED_SEQUENTIAL || p.sched == MMAR_SCHED_STREAMS ||
                           p.sched == MMAR_SCHED_PERSISTENT ||
-                          (p.sched == MMAR_SCHED_BALANCED && p.cm == s.M && p.cn == s.N);
+                          ((p.sched == MMAR_SCHED_BALANCED || p.sched == MMAR_SCHED_SPLIT) &&
+                           p.cm == s.M && p.cn == s.N);
     const bool ring_ok = p.ring >= 0 && p.ring <= kMaxRing &&
                          (p.sched != MMAR_SCHED_STREAMS || p.ring >= 1);
     const bool w_ok = p.wmode == MMAR_W_DIRECT || p.wmode == MMAR_W_PRETRANSPOSE;
@@ -633,6 +635,30 @@ int run_balanced(const DevState* st, const Call& c, const Plan& p, float* ws, hi
                          c.drop, s);
 }
 
+// Split schedule: the persistent kernel over the head block (whole rounds), then the
+// persistent kernel again over the tail on 128 x 128 tiles, twice as many as whole tiles
+// would give, so the tail's round keeps every CU busy for about half as long; the same
+// bits as the persistent schedule (each output's MFMA sequence, slice order and epilogue
+// do not depend on the tile), no workspace.
+int run_split(const DevState* st, const Call& c, const Plan& p, hipStream_t s) {
+    if (p.hm == 0) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s, p.tile);
+    const int M = static_cast<int>(c.s.M), N = static_cast<int>(c.s.N);
+    const int bk = bk_for(c.s);
+    TileArgs a = tile_args(c, 0, 0, p.hm, p.hn, p.hm, p.hn);
+    a.total_items = static_cast<int32_t>(tiles_in(p.hm, p.hn, block_bn(p.tile)));
+    MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, p.tile, a,
+                               grid_for(st, mmar::kModeFused, bk, a.total_items, p.tile), s));
+    const int tr0 = p.hm == M ? 0 : p.hm, tc0 = p.hm == M ? p.hn : 0;
+    const int TM = M - tr0, TN = N - tc0;
+    TileArgs b = tile_args(c, tr0, tc0, TM, TN, TM, TN);
+    b.total_items = static_cast<int32_t>(((TM + mmar::kBMHalf - 1) / mmar::kBMHalf) *
+                                         ((TN + mmar::kBN - 1) / mmar::kBN));
+    MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, mmar::kTileHalf, b,
+                               grid_for(st, mmar::kModeFused, bk, b.total_items, mmar::kTileHalf),
+                               s));
+    return MMAR_OK;
+}
+
 // What a call runs: the fused block (any schedule), or the measurement paths that share
 // its kernels.
 enum RunKind { kRunFused = 0, kRunReduced = 1, kRunPartials = 2 };
@@ -655,6 +681,7 @@ int run_with_ws(DevState* st, Call c, const Plan& p, RunKind kind, char* ws, hip
         return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s, p.tile);
     if (p.sched == MMAR_SCHED_BALANCED)
         return run_balanced(st, c, p, reinterpret_cast<float*>(ws + wt_bytes), s);
+    if (p.sched == MMAR_SCHED_SPLIT) return run_split(st, c, p, s);
     return run_chunked(st, c, p, reinterpret_cast<float*>(ws + wt_bytes), s);
 }
 
@@ -722,8 +749,9 @@ int fused_impl(const uint16_t* X, const uint16_t* W, bool w_t, const uint16_t* b
     int rc = check_call(X, W, bias, residual, out, s, p_drop, seed, chunk_m, chunk_n, &c);
     if (rc) return rc;
     if ((rc = check_sched(sched, ring, wmode, tile))) return rc;
-    if (sched == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
-        return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
+    if ((sched == MMAR_SCHED_BALANCED || sched == MMAR_SCHED_SPLIT) &&
+        ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
+        return fail(MMAR_EINVAL, "the balanced and split schedules take the whole output as one chunk");
     c.w_t = w_t;
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
@@ -752,8 +780,9 @@ int fused_fixed_ws(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
     int rc = check_call(X, W, bias, residual, out, s, p_drop, seed, chunk_m, chunk_n, &c);
     if (rc) return rc;
     if ((rc = check_sched(sched, ring, wmode, tile))) return rc;
-    if (sched == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
-        return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
+    if ((sched == MMAR_SCHED_BALANCED || sched == MMAR_SCHED_SPLIT) &&
+        ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
+        return fail(MMAR_EINVAL, "the balanced and split schedules take the whole output as one chunk");
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     const Plan p = plan_for(st, s, sched, chunk_m, chunk_n, ring, wmode, tile);
@@ -899,8 +928,9 @@ size_t mmar_workspace_bytes(int32_t schedule, int64_t M, int64_t N, int64_t K, i
     if (check_shape(s) || check_chunk(s, chunk_m, chunk_n) ||
         check_sched(schedule, ring, w_mode, tile))
         return 0;
-    if (schedule == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N))) {
-        fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
+    if ((schedule == MMAR_SCHED_BALANCED || schedule == MMAR_SCHED_SPLIT) &&
+        ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N))) {
+        fail(MMAR_EINVAL, "the balanced and split schedules take the whole output as one chunk");
         return 0;
     }
     // the current device's architecture and CU count if the library has seen it
@@ -1360,8 +1390,9 @@ int mmar_set_plan(int64_t M, int64_t N, int64_t K, int32_t P, int32_t schedule,
     if ((rc = check_shape(s)) || (rc = check_chunk(s, chunk_m, chunk_n)) ||
         (rc = check_sched(schedule, ring, w_mode, tile)))
         return rc;
-    if (schedule == MMAR_SCHED_BALANCED && ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
-        return fail(MMAR_EINVAL, "the balanced schedule takes the whole output as one chunk");
+    if ((schedule == MMAR_SCHED_BALANCED || schedule == MMAR_SCHED_SPLIT) &&
+        ((chunk_m && chunk_m != M) || (chunk_n && chunk_n != N)))
+        return fail(MMAR_EINVAL, "the balanced and split schedules take the whole output as one chunk");
     DevState* st = nullptr;
     if ((rc = current_device(&st))) return rc;
     std::lock_guard<std::mutex> lk(g_mu);
@@ -1434,13 +1465,14 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
                     p.tile = tile;
                     cands.push_back(resolve(s, p, st->cus));
                 }
-            if (balanced_split(s, st->cus, block_bn(tile)).first != 0) {
-                Plan p;
-                p.sched = MMAR_SCHED_BALANCED;
-                p.wmode = wm;
-                p.tile = tile;
-                cands.push_back(resolve(s, p, st->cus));
-            }
+            if (balanced_split(s, st->cus, block_bn(tile)).first != 0)
+                for (int sched : {MMAR_SCHED_BALANCED, MMAR_SCHED_SPLIT}) {
+                    Plan p;
+                    p.sched = sched;
+                    p.wmode = wm;
+                    p.tile = tile;
+                    cands.push_back(resolve(s, p, st->cus));
+                }
         }
     if (flags & 1u) {
         for (int cm : divisors32(M, {2, 4, 8, 16}))

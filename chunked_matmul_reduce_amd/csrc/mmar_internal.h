@@ -86,12 +86,19 @@ constexpr int kBM = 256;   // output rows per tile
 constexpr int kBN = 128;   // output columns per tile
 constexpr int kBNWide = 256;   // output columns per tile of kModeLinearWide
 
-// Tile shapes of the block's modes (kModeFused, kModeReduced): the plan's choice.
+// Tile shapes of the block's modes (kModeFused, kModeReduced): the plan's choice, and the
+// half-height tile of the split schedule's tail.
 enum TileShape : int {
     kTile128 = 0,   // 256 x 128: 8 waves of 64 x 64 at BK = 64 (4 waves of 64 x 128 at BK = 32)
     kTile192 = 1,   // 256 x 192: 4 waves of 128 x 96, BK = 32
+    kTileHalf = 2,  // 128 x 128 (kModeFused only): 8 waves of 64 x 32 at BK = 64 (4 waves of
+                    // 64 x 64 at BK = 32); twice as many tiles for a tail region, so a last
+                    // round of whole tiles that would leave CUs idle fills them instead
 };
-constexpr int kNumTiles = 2;
+constexpr int kNumTiles = 3;
+constexpr int kBMHalf = 128;
+// Output rows per tile of a tile shape.
+constexpr int tile_bm(int tile) { return tile == kTileHalf ? kBMHalf : kBM; }
 constexpr int kBN192 = 192;
 // Output columns per tile of a mode on a tile shape (the partials and producer modes
 // have one shape each).
@@ -101,7 +108,9 @@ constexpr int tile_bn(int mode, int tile = kTile128) {
                                                                                : kBN;
 }
 constexpr bool tile_supported(int mode, int tile) {
-    return tile == kTile128 || mode == kModeFused || mode == kModeReduced;
+    return tile == kTile128 ||
+           (tile == kTile192 && (mode == kModeFused || mode == kModeReduced)) ||
+           (tile == kTileHalf && mode == kModeFused);
 }
 
 // Launchers (tile_kernel.hip, reduce_kernels.hip).  bk is 64 or 32 (the K step; it must

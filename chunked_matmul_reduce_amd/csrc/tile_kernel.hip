@@ -74,7 +74,8 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // one slice long (12 % slower with 8 waves), and at BK = 32, where a W stage has too few
 // 16-byte chunks for 8 waves to copy them in pairs.  The 256 x 192 tile has 4 waves, one
 // per SIMD, each holding a 128 x 96 block: its slice sum and running total take 384 of
-// the 512 registers a lone wave has.
+// the 512 registers a lone wave has.  The 128 x 128 tail tile follows the 256 x 128 rule
+// (8 waves of 64 x 32 at BK = 64, 4 of 64 x 64 at BK = 32).
 constexpr int tile_waves(int mode, int bk, int tile) {
     return tile == kTile192 ? 4
            : mode == kModeLinearWide ? 8
@@ -88,9 +89,9 @@ constexpr int tile_bk(int mode, int bk, int tile) {
 constexpr bool is_linear(int mode) { return mode == kModeLinear || mode == kModeLinearWide; }
 
 template <int BK, int NW_, int BN_, int WM_, int LEAD_, int XSTAGES_, int WSTAGES_,
-          int TLDS_ = 0>
+          int TLDS_ = 0, int BM_ = kBM>
 struct TileCfgT {
-    static constexpr int BM = kBM, BN = BN_;
+    static constexpr int BM = BM_, BN = BN_;
     static constexpr int NW = NW_;
     static constexpr int THREADS = 64 * NW;
     static constexpr int WM = WM_;                      // waves along m
@@ -134,8 +135,9 @@ struct TileCfgOf {
     static constexpr int NW = tile_waves(MODE, BK, TILE);
     static constexpr int BN = tile_bn(MODE, TILE);
     static constexpr int LEAD = TILE == kTile192 ? 3 : BK == 64 ? 2 : BN == 256 ? 3 : 5;
-    using type = TileCfgT<BK, NW, BN, TILE == kTile192 ? 2 : 4, LEAD, LEAD + 1,
-                          TILE == kTile192 ? LEAD + 1 : LEAD + 2, TILE == kTile192 ? 3 : 0>;
+    using type = TileCfgT<BK, NW, BN, TILE == kTile128 ? 4 : 2, LEAD, LEAD + 1,
+                          TILE == kTile192 ? LEAD + 1 : LEAD + 2, TILE == kTile192 ? 3 : 0,
+                          tile_bm(TILE)>;
 };
 
 // 16-byte chunk swizzles (bank-conflict-free MFMA operand reads).  X stage rows are BK
@@ -1043,6 +1045,11 @@ static hipError_t launch_tile_w(int mode, int bk, int tile, const TileArgs& a, i
         if (mode == kModeReduced) return launch_tile_t<kModeReduced, 32, WT, kTile192>(a, grid, s);
         return hipErrorInvalidValue;
     }
+    if (tile == kTileHalf) {
+        if (mode != kModeFused) return hipErrorInvalidValue;
+        return bk == 64 ? launch_tile_t<kModeFused, 64, WT, kTileHalf>(a, grid, s)
+                        : launch_tile_t<kModeFused, 32, WT, kTileHalf>(a, grid, s);
+    }
     if (mode == kModeLinearWide) return launch_tile_t<kModeLinearWide, 32, WT, kTile128>(a, grid, s);
     if (bk == 64) {
         if (mode == kModeFused) return launch_tile_t<kModeFused, 64, WT, kTile128>(a, grid, s);
@@ -1079,6 +1086,8 @@ int tile_occupancy(int mode, int bk, int tile) {
     if (tile == kTile192)
         return mode == kModeFused ? occ_t<kModeFused, 32, kTile192>()
                                   : occ_t<kModeReduced, 32, kTile192>();
+    if (tile == kTileHalf)
+        return bk == 64 ? occ_t<kModeFused, 64, kTileHalf>() : occ_t<kModeFused, 32, kTileHalf>();
     if (mode == kModeLinearWide) return occ_t<kModeLinearWide, 32, kTile128>();
     if (bk == 64) {
         if (mode == kModeFused) return occ_t<kModeFused, 64, kTile128>();

@@ -41,6 +41,11 @@
  *                          slice order.  Whole-output chunk only; the tail's partials
  *                          take P x M x (tail columns) x 4 bytes (or P x (tail rows) x
  *                          N x 4) of workspace.  Without such a split it is PERSISTENT.
+ *   MMAR_SCHED_SPLIT       PERSISTENT over the same head block, then PERSISTENT again over
+ *                          the tail on 128 x 128 tiles (twice as many as whole tiles, so
+ *                          their round fills more CUs for half as long); no partials and no
+ *                          workspace.  Whole-output chunk only.  Without a split it is
+ *                          PERSISTENT.
  *
  * Layouts.  X [M,K], W [K,N], residual [M,N] row-major, contiguous, bf16 bit patterns
  * (uint16); bias [N] bf16 bits; out [M,N] row-major fp32.  All tensor pointers are
@@ -106,13 +111,15 @@ enum {
     MMAR_SCHED_SEQUENTIAL = 1,
     MMAR_SCHED_STREAMS = 2,
     MMAR_SCHED_PERSISTENT = 3,
-    MMAR_SCHED_BALANCED = 4
+    MMAR_SCHED_BALANCED = 4,
+    MMAR_SCHED_SPLIT = 5
 };
 
 enum { MMAR_W_AUTO = -1, MMAR_W_DIRECT = 0, MMAR_W_PRETRANSPOSE = 1 };
 
 /* Output tile of the persistent fused kernel (MMAR_SCHED_PERSISTENT, and the head block of
- * MMAR_SCHED_BALANCED; the chunked schedules always use 256 x 128).
+ * MMAR_SCHED_BALANCED and MMAR_SCHED_SPLIT, whose tail always runs on 128 x 128 tiles; the
+ * chunked schedules always use 256 x 128).
  *   MMAR_TILE_256x128  8 waves per workgroup, each a 64 x 64 block of the tile.
  *   MMAR_TILE_256x192  4 waves, each a 128 x 96 block: 42 % fewer operand bytes read from
  *                      LDS and 22 % fewer bytes copied into it per flop; 3 of a wave's 12
@@ -156,7 +163,7 @@ int mmar_fused_bf16(const uint16_t* X, const uint16_t* W, const uint16_t* bias,
 /* Workspace bytes a plan needs: K N 2 (256-aligned) for MMAR_W_PRETRANSPOSE, plus the
  * partial-product ring for MMAR_SCHED_SEQUENTIAL (P chunk_m chunk_n 4) and
  * MMAR_SCHED_STREAMS (ring times that), plus the tail partials of MMAR_SCHED_BALANCED
- * (which depend on the tile).  schedule AUTO: the plan mmar_fused would use (with non-zero
+ * (which depend on the tile); MMAR_SCHED_SPLIT needs none.  schedule AUTO: the plan mmar_fused would use (with non-zero
  * chunk / ring and non-AUTO w_mode / tile arguments overriding).  ring = number of chunk
  * slots for MMAR_SCHED_STREAMS (0 = the default, 2).  Returns 0 and sets the last error on
  * invalid arguments. */

@@ -122,13 +122,28 @@ def test_balanced_schedule_workspace_and_chunk():
         mmar.workspace_bytes("balanced", 8192, 2560, 10240, 8, chunk=(4096, 0))
     L = mmar.lib
     assert L.mmar_set_plan(8192, 2560, 10240, 8, 4, 4096, 0, 0, -1, -1) == mmar.EINVAL
-    assert L.mmar_workspace_bytes(5, 8192, 2560, 10240, 8, 0, 0, 0, -1, -1) == 0
+    assert L.mmar_workspace_bytes(6, 8192, 2560, 10240, 8, 0, 0, 0, -1, -1) == 0
+    assert b"schedule" in L.mmar_last_error()
     # with 256 x 192 tiles: 32 x 14 = 448 tiles; the head is 8192 x 1536 (256 tiles), the
     # tail 8192 x 1024
     assert mmar.workspace_bytes("balanced", 8192, 2560, 10240, 8, tile="256x192") == 8 * 8192 * 1024 * 4
     # 8192 x 3072 on 256 x 192 tiles is 512 tiles: two full rounds, no tail
     assert mmar.workspace_bytes("balanced", 8192, 3072, 12288, 16, tile="256x192") == 0
     assert L.mmar_workspace_bytes(4, 8192, 2560, 10240, 8, 0, 0, 0, -1, 3) == 0
+
+
+def test_split_schedule_needs_no_workspace():
+    """The split schedule's tail runs the fused kernel again on 128 x 128 tiles: no
+    partials, so no workspace (only a pre-transposed weight takes any); whole-output
+    chunk only."""
+    assert mmar.workspace_bytes("split", 8192, 2560, 10240, 8) == 0
+    assert mmar.workspace_bytes("split", 8192, 2560, 10240, 8, tile="256x192") == 0
+    assert mmar.workspace_bytes("split", 8192, 2560, 10240, 8, w_mode="pretranspose") == \
+        10240 * 2560 * 2
+    with pytest.raises(mmar.MmarError):
+        mmar.workspace_bytes("split", 8192, 2560, 10240, 8, chunk=(0, 1280))
+    assert mmar.lib.mmar_set_plan(8192, 2560, 10240, 8, mmar.SCHED_SPLIT, 4096, 0, 0, -1, -1) == \
+        mmar.EINVAL
 
 
 def test_workspace_bytes():

@@ -21,11 +21,13 @@ if not torch.cuda.is_available():  # collected on CPU-only machines, never run t
 import chunked_matmul_reduce_amd as mmar  # noqa: E402
 
 ONE = 0x3F80
-SCHEDS = ["persistent", "sequential", "streams", "balanced"]   # balanced: whole-output chunk only
-# (schedule, tile): the persistent kernel and the balanced schedule's head on both tile
-# shapes; the chunked schedules have one
+# balanced and split: whole-output chunk only
+SCHEDS = ["persistent", "sequential", "streams", "balanced", "split"]
+# (schedule, tile): the persistent kernel and the balanced and split schedules' heads on
+# both tile shapes; the chunked schedules have one
 PLANS = [("persistent", "256x128"), ("persistent", "256x192"), ("sequential", "auto"),
-         ("streams", "auto"), ("balanced", "256x128"), ("balanced", "256x192")]
+         ("streams", "auto"), ("balanced", "256x128"), ("balanced", "256x192"),
+         ("split", "256x128"), ("split", "256x192")]
 
 
 def _to_dev(inp):
@@ -74,7 +76,7 @@ def test_tiny_all_schedules_chunks_bit_identical():
     outs = {}
     for sched, tile in PLANS:
         for chunk in [(32, 64), (64, 64), (32, 256), (64, 256), (0, 0)]:
-            if sched == "balanced" and chunk != (0, 0):
+            if sched in ("balanced", "split") and chunk != (0, 0):
                 continue
             for wm in ("direct", "pretranspose"):
                 out = _run(d, w.P, inp["p_drop"], w.seed, sched, chunk, w_mode=wm, tile=tile)
@@ -113,7 +115,7 @@ def test_ragged_shapes_against_oracle(M, K, N, P):
     print("ragged", M, K, N, P, flush=True)
     for sched, tile in PLANS:
         for chunk in [(0, 0), (32, 32), (M // 2 if (M // 2) % 32 == 0 else M, N)]:
-            if sched == "balanced" and chunk != (0, 0):
+            if sched in ("balanced", "split") and chunk != (0, 0):
                 continue
             for wm in ("direct", "pretranspose"):
                 out = _run(d, P, inp["p_drop"], inp["seed"], sched, chunk, w_mode=wm, tile=tile)
@@ -240,18 +242,20 @@ BALANCED_SPLITS = [(8192, 512, 1088, 4), (2080, 512, 4096, 4), (8192, 10240, 256
 @pytest.mark.parametrize("M,K,N,P", BALANCED_SPLITS)
 def test_balanced_split_bits_and_oracle(M, K, N, P):
     """The balanced schedule (persistent head, tail by slice through partials and the
-    reduce+epilogue kernel) gives the persistent schedule's bits; sampled rows, the tail
-    included, against the oracle."""
+    reduce+epilogue kernel) and the split schedule (persistent head, tail on 128 x 128
+    tiles) give the persistent schedule's bits; sampled rows, the tail included, against
+    the oracle."""
     print("balanced", M, K, N, P, flush=True)
     assert mmar.workspace_bytes("balanced", M, N, K, P) > 0      # the split exists
     inp = make_random_inputs(M, K, N, seed=M + N + P)
     inp.update(M=M, K=K, N=N, P=P, p_drop=np.float32(0.1), seed=(N << 20) + M)
     d = _to_dev(inp)
     ref = _run(d, P, inp["p_drop"], inp["seed"], "persistent", w_mode="direct")
-    for wm in ("direct", "pretranspose"):
-        for tile in ("256x128", "256x192"):
-            out = _run(d, P, inp["p_drop"], inp["seed"], "balanced", w_mode=wm, tile=tile)
-            assert np.array_equal(f32_bits(out), f32_bits(ref)), (wm, tile)
+    for sched in ("balanced", "split"):
+        for wm in ("direct", "pretranspose"):
+            for tile in ("256x128", "256x192"):
+                out = _run(d, P, inp["p_drop"], inp["seed"], sched, w_mode=wm, tile=tile)
+                assert np.array_equal(f32_bits(out), f32_bits(ref)), (sched, wm, tile)
     rng = np.random.default_rng(M + N)
     rows = np.unique(np.concatenate([[0, 255, 256, M - 33, M - 32, M - 1],
                                      rng.choice(M, 40, replace=False)]))

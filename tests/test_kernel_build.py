@@ -6,8 +6,9 @@ needed: hipcc cross-compiles the device code to assembly here).
   correct while the compiler keeps nothing of its own in M0 in these kernels, so the
   assembly must hold no M0 access outside those asm blocks.
 * Registers: the kernels of the default plans (the fused block, GEMM alone, the partials
-  mode and both producer tiles on 256 x 128 / 256 x 256) must run without scratch, and the
-  8-wave ones within 256 registers, so that two waves fit on each SIMD.
+  mode and both producer tiles on 256 x 128 / 256 x 256) and the split schedule's
+  128 x 128 tail tile must run without scratch, and the 8-wave ones within 256 registers,
+  so that two waves fit on each SIMD.
 """
 import os
 import re
@@ -81,7 +82,8 @@ def test_m0_only_inside_the_copy_asm(asm):
 # legs launch, and whether they run 8 waves per workgroup
 DEFAULT_KERNELS = [(0, 64, False, 0, True), (0, 64, True, 0, True), (1, 64, False, 0, True),
                    (1, 64, True, 0, True), (3, 64, False, 0, True), (4, 32, False, 0, True),
-                   (2, 64, False, 0, False), (0, 32, False, 0, False), (0, 32, False, 1, False)]
+                   (2, 64, False, 0, False), (0, 32, False, 0, False), (0, 32, False, 1, False),
+                   (0, 64, False, 2, True), (0, 32, False, 2, False)]
 
 
 @pytest.mark.parametrize("mode,bk,wt,tile,eight", DEFAULT_KERNELS)
