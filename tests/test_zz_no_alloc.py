@@ -23,6 +23,9 @@ CASES = [
     ("persistent", "256x192", "pretranspose", 0, (1024, 2048, 1536, 8), (512, 1024, 384, 4)),
     ("persistent", "256x128", "pretranspose", 0, (768, 1024, 640, 4), (256, 256, 256, 1)),
     ("balanced", "256x128", "direct", 0, (2080, 512, 8192, 4), (2080, 512, 4096, 4)),
+    # the split schedule needs workspace only for the pre-transposed weight; its first
+    # shape has a tail (288 tiles on 256 CUs), its second none
+    ("split", "256x128", "pretranspose", 0, (2080, 512, 4096, 4), (1056, 256, 1024, 2)),
 ]
 
 
