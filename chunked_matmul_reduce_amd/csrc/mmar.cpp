@@ -615,21 +615,36 @@ int run_chunked(DevState* st, const Call& c, const Plan& p, float* ws, hipStream
     return MMAR_OK;
 }
 
-// Balanced schedule: the persistent kernel over the head block (whole rounds), then the
-// tail's one-slice partials spread over every CU and the reduce+epilogue kernel over the
-// tail; the same bits as the persistent schedule (the same MFMA sequence per slice, the
-// same fixed-order fp32 reduction and epilogue).
-int run_balanced(const DevState* st, const Call& c, const Plan& p, float* ws, hipStream_t s) {
-    if (p.hm == 0) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s, p.tile);
+// The persistent fused kernel over the head block [0, hm) x [0, hn) of a balanced or split
+// plan; the tail region [tr0, M) x [tc0, N) is left to the caller.
+struct Tail {
+    int tr0, tc0, TM, TN;
+};
+int launch_head(const DevState* st, const Call& c, const Plan& p, hipStream_t s, Tail* tail) {
     const int M = static_cast<int>(c.s.M), N = static_cast<int>(c.s.N);
     const int bk = bk_for(c.s);
     TileArgs a = tile_args(c, 0, 0, p.hm, p.hn, p.hm, p.hn);
     a.total_items = static_cast<int32_t>(tiles_in(p.hm, p.hn, block_bn(p.tile)));
     MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, p.tile, a,
                                grid_for(st, mmar::kModeFused, bk, a.total_items, p.tile), s));
-    const int tr0 = p.hm == M ? 0 : p.hm, tc0 = p.hm == M ? p.hn : 0;
-    const int TM = M - tr0, TN = N - tc0;
-    int rc = launch_partials(st, c, tr0, tc0, TM, TN, ws, s);
+    tail->tr0 = p.hm == M ? 0 : p.hm;
+    tail->tc0 = p.hm == M ? p.hn : 0;
+    tail->TM = M - tail->tr0;
+    tail->TN = N - tail->tc0;
+    return MMAR_OK;
+}
+
+// Balanced schedule: the persistent kernel over the head block (whole rounds), then the
+// tail's one-slice partials spread over every CU and the reduce+epilogue kernel over the
+// tail; the same bits as the persistent schedule (the same MFMA sequence per slice, the
+// same fixed-order fp32 reduction and epilogue).
+int run_balanced(const DevState* st, const Call& c, const Plan& p, float* ws, hipStream_t s) {
+    if (p.hm == 0) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s, p.tile);
+    Tail tl;
+    int rc = launch_head(st, c, p, s, &tl);
+    if (rc) return rc;
+    const int tr0 = tl.tr0, tc0 = tl.tc0, TM = tl.TM, TN = tl.TN;
+    rc = launch_partials(st, c, tr0, tc0, TM, TN, ws, s);
     if (rc) return rc;
     return launch_reduce(st, ws, c.bias, c.residual, c.out, c.s.N, c.s.P, tr0, tc0, TM, TN,
                          c.drop, s);
@@ -642,17 +657,13 @@ int run_balanced(const DevState* st, const Call& c, const Plan& p, float* ws, hi
 // do not depend on the tile), no workspace.
 int run_split(const DevState* st, const Call& c, const Plan& p, hipStream_t s) {
     if (p.hm == 0) return run_persistent(st, c, mmar::kModeFused, p.cm, p.cn, s, p.tile);
-    const int M = static_cast<int>(c.s.M), N = static_cast<int>(c.s.N);
+    Tail tl;
+    int rc = launch_head(st, c, p, s, &tl);
+    if (rc) return rc;
     const int bk = bk_for(c.s);
-    TileArgs a = tile_args(c, 0, 0, p.hm, p.hn, p.hm, p.hn);
-    a.total_items = static_cast<int32_t>(tiles_in(p.hm, p.hn, block_bn(p.tile)));
-    MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, p.tile, a,
-                               grid_for(st, mmar::kModeFused, bk, a.total_items, p.tile), s));
-    const int tr0 = p.hm == M ? 0 : p.hm, tc0 = p.hm == M ? p.hn : 0;
-    const int TM = M - tr0, TN = N - tc0;
-    TileArgs b = tile_args(c, tr0, tc0, TM, TN, TM, TN);
-    b.total_items = static_cast<int32_t>(((TM + mmar::kBMHalf - 1) / mmar::kBMHalf) *
-                                         ((TN + mmar::kBN - 1) / mmar::kBN));
+    TileArgs b = tile_args(c, tl.tr0, tl.tc0, tl.TM, tl.TN, tl.TM, tl.TN);
+    b.total_items = static_cast<int32_t>(((tl.TM + mmar::kBMHalf - 1) / mmar::kBMHalf) *
+                                         ((tl.TN + mmar::kBN - 1) / mmar::kBN));
     MMAR_HIP(mmar::launch_tile(mmar::kModeFused, bk, c.w_t, mmar::kTileHalf, b,
                                grid_for(st, mmar::kModeFused, bk, b.total_items, mmar::kTileHalf),
                                s));
