@@ -41,6 +41,9 @@ its first launches; the timed steps then run at the sustained clock.
                  the vendor yardstick, for its kernel trace
 --only tune      autotune the four block workloads and print the plans chosen (with
                  MMAR_PLAN_CACHE set, the cache file also records each plan's margin)
+--only hbm       time only the HBM-bound kernels (the reduce+epilogue over the workload's
+                 P materialized partials, the epilogue alone, the reduce + Adam step), for
+                 their kernel traces and byte counters
 """
 import argparse
 import hashlib
@@ -277,7 +280,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gpt2_mlp")
     ap.add_argument("--only", choices=["all", "fused", "streams", "producer", "copy", "vendor",
-                                       "tune"],
+                                       "tune", "hbm"],
                     default="all")
     ap.add_argument("--cpu-budget", type=float, default=30.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -354,6 +357,41 @@ def main():
         def fused():
             mmar.fused_ex(X, W, bias, res, P, p, seed, "persistent", w_mode="direct", tile=args.tile,
                           out=out)
+
+    if args.only == "hbm":
+        # the HBM-bound kernels alone, for their kernel traces and byte counters: the
+        # reduce+epilogue over the P materialized slice partials of the workload, the
+        # epilogue alone over a materialized T (P = 1), and the data-parallel reduce + Adam
+        # step over BERT-large's parameters
+        parts = torch.empty((P, w.M, w.N), dtype=torch.float32, device="cuda")
+        mmar.gemm_partials(X, W, P, out=parts)
+        T = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        mmar.gemm_only(X, W, P, out=T)
+        res_hbm = {"only": "hbm", "workload": w.name, "steps": args.steps}
+        legs = {"reduce_epilogue": (lambda: mmar.reduce_epilogue_only(parts, bias, res, p, seed, out=out),
+                                    (4 * P + 6) * w.M * w.N + 2 * w.N),
+                "epilogue": (lambda: mmar.reduce_epilogue_only(T[None], bias, res, p, seed, out=out),
+                             10 * w.M * w.N + 2 * w.N)}
+        aw = ADAM_WORKLOADS["bert_large_adam"]
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(aw.seed)
+        ag = torch.randn((aw.P, aw.n), generator=gen, device="cuda").mul_(1e-2)
+        ap_ = torch.randn(aw.n, generator=gen, device="cuda").mul_(0.02)
+        am = torch.randn(aw.n, generator=gen, device="cuda").mul_(1e-3)
+        av = am.mul(2).square()
+        apb = torch.empty(aw.n, dtype=torch.bfloat16, device="cuda")
+        legs["adam"] = (lambda: mmar.adam_step(ag, ap_, am, av, aw.step, aw.lr, aw.beta1, aw.beta2,
+                                               aw.eps, aw.weight_decay, param_bf16=apb), aw.bytes)
+        for name, (fn, nbytes) in legs.items():
+            for _ in range(args.warmup):
+                fn()
+            torch.cuda.synchronize()
+            med = _ev_time(torch, fn, args.steps)[0]
+            res_hbm[name] = {"median_us": round(med * 1e3, 2), "bytes": int(nbytes),
+                             "GB/s": round(nbytes / (med * 1e-3) / 1e9, 1),
+                             "frac_hbm": round(nbytes / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+        print(json.dumps(res_hbm), flush=True)
+        return
 
     if args.only == "vendor":
         Cv = torch.empty((w.M, w.N), dtype=torch.bfloat16, device="cuda")
