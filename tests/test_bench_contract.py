@@ -31,7 +31,7 @@ def test_traffic_summary_matches_its_workload():
     assert abs(cal["write_factor"] - kib / cal["write_size_kib"]) < 1e-3
     # the request-counter derivation: bytes are requests times their sizes, the copy of
     # 1 GiB reads and writes 1 GiB, and the fused kernel's figure agrees with the calibrated
-    # one within the box-to-box spread
+    # one within the machine-to-machine spread
     rq = d["request_counters"]
     f = rq["fused"]
     assert f["read_bytes_per_launch"] == (128 * f["TCC_EA0_RDREQ_128B"] + 64 * f["TCC_EA0_RDREQ_64B"]
