@@ -1553,11 +1553,11 @@ int mmar_autotune(int64_t M, int64_t N, int64_t K, int32_t P, uint32_t flags) {
     // challenger qualifies only if its median beats the incumbent's by more than the
     // larger of the two interquartile ranges and by at least kMinGain of the incumbent's
     // median (a win inside the run-to-run spread, or one too small to matter, would flip
-    // from one run or box to the next).  Among the qualifying challengers, those whose
+    // from one run or machine to the next).  Among the qualifying challengers, those whose
     // medians lie within the larger interquartile range of the fastest one's are a tie,
     // and the tie goes to the earliest in candidate order (larger chunks, W read
     // directly, the 256 x 128 tile first), so that near-equal plans do not trade places
-    // from box to box.
+    // from machine to machine.
     constexpr int kTuneRounds = 25, kTuneBatch = 4;
     constexpr float kMinGain = 0.01f;
     std::vector<std::vector<float>> times;
