@@ -234,6 +234,29 @@ def test_full_size_schedule_invariance():
         assert np.array_equal(f32_bits(out), ref), (sched, chunk, ring, wm, tile)
 
 
+@pytest.mark.parametrize("name,sched,tile,chunk,ring", [
+    ("gpt2_mlp", "persistent", "256x128", (0, 0), 0),
+    ("gpt2_mlp", "persistent", "256x192", (0, 0), 0),
+    ("bert_mlp", "split", "256x128", (0, 0), 0),
+    ("gpt2_attn", "streams", "auto", (1024, 3072), 2)])
+def test_repeated_launches_bit_identical(name, sched, tile, chunk, ring):
+    """Twenty back-to-back launches of one full-size call, each into its own output, give
+    the same bits every time: a race in the LDS ring's handshake, in the next item's copies
+    issued under the epilogue or in the two-stream schedule's event ring would show as a
+    launch that differs."""
+    w = WORKLOADS[name]
+    inp = make_inputs(name)
+    d = _to_dev(inp)
+    print(name, sched, tile, chunk, ring, flush=True)
+    outs = [mmar.fused_ex(d["X"], d["W"], d["bias"], d["residual"], w.P, inp["p_drop"], w.seed,
+                          sched, chunk=chunk, ring=ring, w_mode="direct", tile=tile)
+            for _ in range(20)]
+    torch.cuda.synchronize()
+    ref = outs[0].view(torch.int32)
+    for i, o in enumerate(outs[1:], 1):
+        assert torch.equal(o.view(torch.int32), ref), (name, sched, tile, i)
+
+
 # (M, K, N, P) with a head of whole rounds on 256 CUs and a tail: one ragged tile column,
 # one ragged tile row, and the BERT-shaped block (512 + 128 tiles)
 BALANCED_SPLITS = [(8192, 512, 1088, 4), (2080, 512, 4096, 4), (8192, 10240, 2560, 8)]
